@@ -1,0 +1,291 @@
+"""Benchmark of the DLRMv1 forward hot path on one MI355X.
+
+One step = one call of dlrm_forward (bottom MLP, bag gather + interaction,
+top MLP, sigmoid) over one batch of seeded synthetic inputs already resident
+in HBM.  Steps cycle through --index-sets independently drawn index sets so
+that consecutive steps gather different rows.  By default the steps are
+replayed from HIP graphs (captured once, outside the timed region) so that
+host launch overhead does not hide the kernels; --eager times plain calls.
+
+Printed: one JSON line with the contract fields, plus
+  roofline          the dominant kernel of a step against its roofline,
+                    from a live HIP-event timing of that kernel;
+  roofline_emb_interact  the same for the fused bag-gather + interaction kernel;
+  kernels           per-stage average durations (HIP events);
+  cpu_baseline      the fp64 oracle timed on the host cores on a bounded
+                    sample of the workload;
+  secondary         the 32-table workload (bs 2048) when --secondary is given.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, GB/s
+FP32_MFMA_PEAK_TFLOPS = 157.3   # MI355X dense fp32 matrix
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=400)
+    p.add_argument("--warmup", type=int, default=40)
+    p.add_argument("--workload", default="page4")
+    p.add_argument("--index-sets", type=int, default=8)
+    p.add_argument("--eager", action="store_true", help="time plain calls instead of graph replays")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--secondary", action="store_true", help="also time the 32-table workload")
+    p.add_argument("--kernel-reps", type=int, default=50)
+    return p.parse_args()
+
+
+def algorithmic(w):
+    """Algorithmic bytes / flops per launch of each stage (what the method must move or compute)."""
+    B, T, D, L = w.batch, w.num_tables, w.dim, w.bag
+    P = w.n_pairs
+    stages = []
+    ln = list(w.ln_bot)
+    for l in range(len(ln) - 1):
+        K, N = ln[l], ln[l + 1]
+        stages.append(dict(name=f"bot{l}", kind="mfma" if N > 1 else "hbm", flops=2 * B * N * K,
+                           bytes=4 * (B * K + N * K + N + B * N), M=B, N=N, K=K))
+    # fused gather + interaction: rows, indices, offsets, x read, Z written
+    emb_bytes = B * T * L * (D * 4 + 8) + B * T * 8 + B * D * 4 + B * P * 4
+    stages.append(dict(name="emb_interact", kind="hbm", flops=2 * B * P * D, bytes=emb_bytes))
+    ln = list(w.ln_top)
+    for l in range(len(ln) - 1):
+        K, N = ln[l], ln[l + 1]
+        stages.append(dict(name=f"top{l}", kind="mfma" if N > 1 else "hbm", flops=2 * B * N * K,
+                           bytes=4 * (B * K + N * K + N + B * N), M=B, N=N, K=K))
+    return stages
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this build measures one GPU only; --gpus must be 1 "
+              "(the forward shards by batch with no exchange, see the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import dlrm_embedding_interaction_amd as dl
+    import dlrm_inputs as di
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dl.load(build_if_missing=False)
+    dev = torch.device("cuda", 0)
+    w = di.get(args.workload)
+
+    res = run_workload(torch, dl, di, w, dev, args)
+    out = {
+        "metric": "DLRMv1 fwd µs @bs2048 nc=3/32; samples/s; emb-bag+interact HBM GB/s",
+        "value": res["samples_per_s"],
+        "unit": "samples/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": res["ms_per_step"],
+        "us_per_forward": res["ms_per_step"] * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded; dense U[0,1), tables N(0,1/D), uniform indices, bag 1)",
+        "config": {"workload": w.name, "batch": w.batch, "num_tables": w.num_tables, "rows_per_table": w.rows,
+                   "dim": w.dim, "bag": w.bag, "ln_bot": list(w.ln_bot), "ln_top": list(w.ln_top),
+                   "mode": "eager" if args.eager else "hip_graph", "index_sets": args.index_sets},
+        "roofline": res["roofline"],
+        "roofline_emb_interact": res["roofline_emb"],
+        "emb_interact_GBps": res["roofline_emb"]["achieved"],
+        "kernels": res["kernels"],
+    }
+    if args.secondary:
+        w2 = di.MANYTABLE
+        r2 = run_workload(torch, dl, di, w2, dev, args)
+        out["secondary"] = {w2.name: {"us_per_forward": r2["ms_per_step"] * 1e3,
+                                      "samples_per_s": r2["samples_per_s"],
+                                      "emb_interact_GBps": r2["roofline_emb"]["achieved"],
+                                      "roofline": r2["roofline"], "roofline_emb_interact": r2["roofline_emb"]}}
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def run_workload(torch, dl, di, w, dev, args):
+    torch.cuda.synchronize()
+    print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)
+    inp = di.make_inputs(w, device=dev)
+    model = dl.Model.from_inputs(inp)
+    B = w.batch
+    nsets = max(1, args.index_sets)
+    idx_sets = [inp.indices]
+    for s in range(1, nsets):
+        idx_sets.append(di.make_indices(w, device=dev, seed=di.BASE_SEED + 7919 * s))
+    ws = model.workspace(B)
+    out = torch.empty(B, device=dev)
+    argsets = [model.forward_args(inp.dense, idx, inp.offsets) for idx in idx_sets]
+
+    def step(i):
+        model.forward(inp.dense, idx_sets[i % nsets], inp.offsets, out=out, workspace=ws, args=argsets[i % nsets])
+
+    for i in range(nsets):
+        step(i)
+    torch.cuda.synchronize()
+
+    run = step
+    if not args.eager:
+        stream = torch.cuda.Stream()
+        graphs = []
+        stream.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(stream):
+            for i in range(nsets):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=stream):
+                    step(i)
+                graphs.append(g)
+        torch.cuda.current_stream().wait_stream(stream)
+        torch.cuda.synchronize()
+
+        def run(i):
+            graphs[i % nsets].replay()
+
+    for i in range(args.warmup):
+        run(i)
+    torch.cuda.synchronize()
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        run(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / args.steps
+
+    kernels = time_stages(torch, dl, model, inp, idx_sets, ws, w, args.kernel_reps)
+    roof = roofline(kernels, dominant=True)
+    roof_emb = roofline([k for k in kernels if k["name"] == "emb_interact"], dominant=True)
+    del inp, model, idx_sets, ws, argsets
+    torch.cuda.empty_cache()
+    return dict(ms_per_step=ms, samples_per_s=B / (ms * 1e-3), kernels=kernels, roofline=roof, roofline_emb=roof_emb)
+
+
+def time_stages(torch, dl, model, inp, idx_sets, ws, w, reps):
+    """Average duration of each stage's kernel, launched alone on the current stream, with HIP events."""
+    stages = algorithmic(w)
+    B, D = w.batch, w.dim
+    P = w.n_pairs
+    ldR = (D + P + 3) // 4 * 4
+    hidden = list(w.ln_bot[1:-1]) + list(w.ln_top[1:-1])
+    ldH = (max(hidden) + 3) // 4 * 4 if hidden else 4
+    dev = inp.dense.device
+    R = torch.zeros((B, ldR), device=dev)
+    H = [torch.zeros((B, ldH), device=dev), torch.zeros((B, ldH), device=dev)]
+    y = torch.empty((B, 1), device=dev)
+    calls = {}
+    h, hsel = inp.dense, 0
+    for l, (W, b) in enumerate(zip(model.bot_w, model.bot_b)):
+        last = l == len(model.bot_w) - 1
+        o = R[:, :W.shape[0]] if last else H[hsel][:, :W.shape[0]]
+        calls[f"bot{l}"] = (lambda h=h, W=W, b=b, o=o: dl.linear_bias_act(h, W, b, dl.ACT_RELU, out=o))
+        if not last:
+            hsel ^= 1
+        h = o
+    nsets = len(idx_sets)
+    cnt = [0]
+
+    def emb():
+        cnt[0] += 1
+        dl.embbag_interact(model.tables, idx_sets[cnt[0] % nsets], inp.offsets, R, concat_dense=False,
+                           out=R[:, D:])
+    calls["emb_interact"] = emb
+    h = R[:, :D + P]
+    for l, (W, b) in enumerate(zip(model.top_w, model.top_b)):
+        last = l == len(model.top_w) - 1
+        o = y if last else H[hsel][:, :W.shape[0]]
+        act = dl.ACT_SIGMOID if last else dl.ACT_RELU
+        calls[f"top{l}"] = (lambda h=h, W=W, b=b, o=o, act=act: dl.linear_bias_act(h, W, b, act, out=o))
+        if not last:
+            hsel ^= 1
+        h = o
+    out = []
+    stream = torch.cuda.Stream()
+    for st in stages:
+        f = calls[st["name"]]
+        for _ in range(3):
+            f()
+        torch.cuda.synchronize()
+        # `reps` launches of this stage alone, captured once and replayed, so
+        # that the events time the GPU work rather than the host call path
+        g = torch.cuda.CUDAGraph()
+        stream.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(stream):
+            with torch.cuda.graph(g, stream=stream):
+                for _ in range(reps):
+                    f()
+        torch.cuda.current_stream().wait_stream(stream)
+        g.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(3):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (3 * reps)
+        d = dict(st)
+        d["us"] = us
+        out.append(d)
+        del g
+    return out
+
+
+def roofline(kernels, dominant=True):
+    k = max(kernels, key=lambda s: s["us"])
+    sec = k["us"] * 1e-6
+    if k["kind"] == "mfma":
+        achieved = k["flops"] / sec / 1e12
+        return {"kernel": k["name"], "bound": "mfma", "achieved": achieved, "peak": FP32_MFMA_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / FP32_MFMA_PEAK_TFLOPS, "traffic": None,
+                "us_per_launch": k["us"], "flops_per_launch": k["flops"],
+                "shape": [k.get("M"), k.get("N"), k.get("K")]}
+    achieved = k["bytes"] / sec / 1e9
+    return {"kernel": k["name"], "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBPS, "traffic": None, "us_per_launch": k["us"],
+            "bytes_per_launch": k["bytes"]}
+
+
+def cpu_baseline(w, seconds):
+    """The fp64 oracle (as it stands) on the host cores, on whole batches until `seconds` have passed."""
+    import oracle
+    import dlrm_inputs as di
+    import torch
+    o = oracle.default()
+    threads = o.set_threads(int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1)))
+    n = min(w.batch, 512)
+    inp = di.make_inputs(w)
+    sub = di.subset(inp, torch.arange(n))
+    done = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.forward_inputs(sub, oracle=o)
+        done += n
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": done / el, "unit": "samples/s", "cores": threads, "kind": "oracle",
+            "sample": f"{w.name}: the first {n} samples of the batch, forward repeated {done // n} times "
+                      f"in {el:.1f} s (fp64, OpenMP over samples)"}
+
+
+if __name__ == "__main__":
+    main()

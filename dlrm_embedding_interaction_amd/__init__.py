@@ -1,0 +1,335 @@
+"""Python binding of libdlrm_mi355x.so, the MI355X (gfx950) DLRMv1 forward hot path.
+
+Thin ctypes marshalling over the C ABI declared in ``include/dlrm_mi355x.h``:
+every step of the computation runs in the library's HIP kernels.  PyTorch is
+used only to hold device memory and to name the current HIP stream.  The
+binding never falls back to another implementation: if the library is missing
+or a call fails, it raises.
+
+Functions take CUDA (HIP) torch tensors:
+
+* ``embbag_sum(tables, indices, offsets)`` -> (B, T, D)
+* ``interact_lower_tri(x, emb, concat_dense=True)`` -> (B, D + P) or (B, P)
+* ``linear_bias_act(x, W, bias, act)`` -> (M, N)
+* ``Model(...)`` holding DLRMv1 parameters, with ``forward(dense, indices, offsets)``
+* ``check_indices(...)``, ``pair_index_map(F)``, ``workspace_bytes``
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Optional, Sequence
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(HERE, "libdlrm_mi355x.so")
+
+DLRM_OK, DLRM_E_NULL, DLRM_E_SHAPE, DLRM_E_WORKSPACE, DLRM_E_UNSUPPORTED, DLRM_E_HIP, DLRM_E_INDEX = range(7)
+ACT_NONE, ACT_RELU, ACT_SIGMOID = 0, 1, 2
+MAX_TABLES = 64
+ABI_VERSION = 1
+
+_i64p = ctypes.POINTER(ctypes.c_int64)
+_vp = ctypes.c_void_p
+
+
+class DlrmError(RuntimeError):
+    def __init__(self, code: int, what: str, msg: str):
+        super().__init__(f"{what}: {msg}")
+        self.code = code
+
+
+class _Model(ctypes.Structure):
+    _fields_ = [
+        ("n_bot", ctypes.c_int32), ("ln_bot", _i64p),
+        ("n_top", ctypes.c_int32), ("ln_top", _i64p),
+        ("num_tables", ctypes.c_int32), ("emb_dim", ctypes.c_int32),
+        ("rows", _i64p),
+        ("emb_w", ctypes.POINTER(_vp)),
+        ("bot_w", ctypes.POINTER(_vp)), ("bot_b", ctypes.POINTER(_vp)),
+        ("top_w", ctypes.POINTER(_vp)), ("top_b", ctypes.POINTER(_vp)),
+    ]
+
+
+_LIB = None
+
+
+def library_path() -> str:
+    return LIBRARY
+
+
+def load(build_if_missing: bool = True) -> ctypes.CDLL:
+    """Load the HIP library (building it with hipcc only if it does not exist)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(LIBRARY):
+        if not build_if_missing:
+            raise ImportError(f"{LIBRARY} is not built")
+        from . import _build
+        _build.build_library()
+    L = ctypes.CDLL(LIBRARY)
+    L.dlrm_status_string.argtypes = [ctypes.c_int]
+    L.dlrm_status_string.restype = ctypes.c_char_p
+    L.dlrm_abi_version.argtypes = []
+    L.dlrm_abi_version.restype = ctypes.c_int32
+    L.dlrm_embbag_sum.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.POINTER(_vp), _i64p,
+                                  ctypes.POINTER(_vp), _i64p, ctypes.POINTER(_vp), _vp, _vp]
+    L.dlrm_interact_lower_tri.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _vp, ctypes.c_int64,
+                                          _vp, _vp, ctypes.c_int64, ctypes.c_int32, _vp]
+    L.dlrm_embbag_interact.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.POINTER(_vp), _i64p,
+                                       ctypes.POINTER(_vp), _i64p, ctypes.POINTER(_vp), _vp, ctypes.c_int64, _vp,
+                                       ctypes.c_int64, ctypes.c_int32, _vp]
+    L.dlrm_linear_bias_act.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _vp, ctypes.c_int64, _vp,
+                                       _vp, ctypes.c_int32, _vp, ctypes.c_int64, _vp]
+    L.dlrm_forward_workspace_bytes.argtypes = [ctypes.POINTER(_Model), ctypes.c_int64]
+    L.dlrm_forward_workspace_bytes.restype = ctypes.c_size_t
+    L.dlrm_forward.argtypes = [ctypes.POINTER(_Model), ctypes.c_int64, _vp, ctypes.POINTER(_vp), _i64p,
+                               ctypes.POINTER(_vp), _vp, _vp, ctypes.c_size_t, _vp]
+    L.dlrm_embbag_check_indices.argtypes = [ctypes.c_int32, ctypes.c_int64, _i64p, ctypes.POINTER(_vp), _i64p,
+                                            ctypes.POINTER(_vp), _vp, _vp]
+    L.dlrm_pair_index_map.argtypes = [ctypes.c_int32, _vp, _vp, _vp]
+    for f in ("dlrm_embbag_sum", "dlrm_interact_lower_tri", "dlrm_embbag_interact", "dlrm_linear_bias_act", "dlrm_forward",
+              "dlrm_embbag_check_indices", "dlrm_pair_index_map"):
+        getattr(L, f).restype = ctypes.c_int
+    if L.dlrm_abi_version() != ABI_VERSION:
+        raise ImportError(f"{LIBRARY}: ABI version {L.dlrm_abi_version()} != {ABI_VERSION}")
+    _LIB = L
+    return L
+
+
+def _check(rc: int, what: str):
+    if rc != DLRM_OK:
+        msg = load().dlrm_status_string(rc).decode()
+        raise DlrmError(rc, what, msg)
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _dev(t: torch.Tensor, dtype: torch.dtype, name: str) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _ptrs(ts: Sequence[torch.Tensor]):
+    return (_vp * max(len(ts), 1))(*[t.data_ptr() for t in ts])
+
+
+def _i64s(vs: Sequence[int]):
+    return (ctypes.c_int64 * max(len(vs), 1))(*[int(v) for v in vs])
+
+
+# --- the four hot-path calls -----------------------------------------------------
+
+
+def embbag_sum(tables: List[torch.Tensor], indices: List[torch.Tensor], offsets: List[torch.Tensor],
+               out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Sum-pooled bags of every table in one launch -> (B, T, D) fp32."""
+    L = load()
+    T = len(tables)
+    if not (T == len(indices) == len(offsets)) or T == 0:
+        raise ValueError("tables, indices and offsets must have the same non-zero length")
+    for i, t in enumerate(tables):
+        _dev(t, torch.float32, f"tables[{i}]")
+        _dev(indices[i], torch.int64, f"indices[{i}]")
+        _dev(offsets[i], torch.int64, f"offsets[{i}]")
+    D = tables[0].shape[1]
+    B = offsets[0].shape[0]
+    if out is None:
+        out = torch.empty((B, T, D), device=tables[0].device, dtype=torch.float32)
+    _dev(out, torch.float32, "out")
+    if tuple(out.shape) != (B, T, D) or any(t.shape[1] != D for t in tables) or any(o.shape[0] != B for o in offsets):
+        raise ValueError("shape mismatch")
+    rc = L.dlrm_embbag_sum(T, B, D, _ptrs(tables), _i64s([t.shape[0] for t in tables]), _ptrs(indices),
+                           _i64s([i.numel() for i in indices]), _ptrs(offsets), out.data_ptr(), _stream(out.device))
+    _check(rc, "dlrm_embbag_sum")
+    return out
+
+
+def n_pairs(n_feat: int) -> int:
+    return n_feat * (n_feat - 1) // 2
+
+
+def interact_lower_tri(x: torch.Tensor, emb: torch.Tensor, concat_dense: bool = True,
+                       out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Strict-lower-triangle dots over [x, emb[:, 0], ...] -> [x | Z] (or Z)."""
+    L = load()
+    if x.dim() != 2 or emb.dim() != 3:
+        raise ValueError("x must be (B, >=D) and emb (B, T, D)")
+    B, T, D = emb.shape
+    if x.device.type != "cuda" or x.dtype != torch.float32 or x.stride(1) != 1 or x.shape[0] != B or x.shape[1] < D:
+        raise ValueError("x must be a (B, >=D) fp32 CUDA tensor with unit column stride")
+    _dev(emb, torch.float32, "emb")
+    P = n_pairs(T + 1)
+    width = D + P if concat_dense else P
+    if out is None:
+        out = torch.empty((B, width), device=emb.device, dtype=torch.float32)
+    if out.dtype != torch.float32 or out.stride(1) != 1 or out.shape[0] != B or out.shape[1] < width:
+        raise ValueError("out must be (B, >= width) fp32 with unit column stride")
+    rc = L.dlrm_interact_lower_tri(B, T, D, x.data_ptr(), x.stride(0), emb.data_ptr(), out.data_ptr(),
+                                   out.stride(0), int(bool(concat_dense)), _stream(emb.device))
+    _check(rc, "dlrm_interact_lower_tri")
+    return out
+
+
+def embbag_interact(tables: List[torch.Tensor], indices: List[torch.Tensor], offsets: List[torch.Tensor],
+                    x: torch.Tensor, concat_dense: bool = True, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Bags gathered and dotted in one launch -> [x | Z] (or Z); E is never materialised."""
+    L = load()
+    T = len(tables)
+    if not (T == len(indices) == len(offsets)) or T == 0:
+        raise ValueError("tables, indices and offsets must have the same non-zero length")
+    for i, t in enumerate(tables):
+        _dev(t, torch.float32, f"tables[{i}]")
+        _dev(indices[i], torch.int64, f"indices[{i}]")
+        _dev(offsets[i], torch.int64, f"offsets[{i}]")
+    D = tables[0].shape[1]
+    B = offsets[0].shape[0]
+    if x.dim() != 2 or x.dtype != torch.float32 or x.stride(1) != 1 or x.shape[0] != B or x.shape[1] < D:
+        raise ValueError("x must be a (B, >=D) fp32 CUDA tensor with unit column stride")
+    P = n_pairs(T + 1)
+    width = D + P if concat_dense else P
+    if out is None:
+        out = torch.empty((B, width), device=x.device, dtype=torch.float32)
+    if out.dtype != torch.float32 or out.stride(1) != 1 or out.shape[0] != B or out.shape[1] < width:
+        raise ValueError("out must be (B, >= width) fp32 with unit column stride")
+    rc = L.dlrm_embbag_interact(T, B, D, _ptrs(tables), _i64s([t.shape[0] for t in tables]), _ptrs(indices),
+                                _i64s([i.numel() for i in indices]), _ptrs(offsets), x.data_ptr(), x.stride(0),
+                                out.data_ptr(), out.stride(0), int(bool(concat_dense)), _stream(x.device))
+    _check(rc, "dlrm_embbag_interact")
+    return out
+
+
+def linear_bias_act(x: torch.Tensor, W: torch.Tensor, bias: Optional[torch.Tensor], act: int,
+                    out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """act(x W^T + bias) with W (N, K) -> (M, N) fp32."""
+    L = load()
+    if x.dim() != 2 or x.stride(1) != 1 or x.dtype != torch.float32 or x.device.type != "cuda":
+        raise ValueError("x must be a 2-D fp32 CUDA tensor with unit column stride")
+    _dev(W, torch.float32, "W")
+    M, K = x.shape
+    N = W.shape[0]
+    if W.shape[1] != K:
+        raise ValueError("W must be (N, K)")
+    if bias is not None:
+        _dev(bias, torch.float32, "bias")
+        if bias.numel() != N:
+            raise ValueError("bias must have N elements")
+    if out is None:
+        out = torch.empty((M, N), device=x.device, dtype=torch.float32)
+    if out.dtype != torch.float32 or out.stride(1) != 1 or tuple(out.shape[:1]) != (M,) or out.shape[1] < N:
+        raise ValueError("out must be (M, >= N) fp32 with unit column stride")
+    rc = L.dlrm_linear_bias_act(M, N, K, x.data_ptr(), x.stride(0), W.data_ptr(),
+                                bias.data_ptr() if bias is not None else None, int(act), out.data_ptr(),
+                                out.stride(0), _stream(x.device))
+    _check(rc, "dlrm_linear_bias_act")
+    return out
+
+
+class Model:
+    """DLRMv1 parameters resident on one GPU, with the fused ``forward``.
+
+    ``tables`` T x (V_t, D); ``bot_w[l]`` (out, in) and ``bot_b[l]``; same for
+    the top MLP, whose last layer has one output.  The descriptor passed to
+    the library is built once; tensors are kept alive by this object.
+    """
+
+    def __init__(self, tables, bot_w, bot_b, top_w, top_b, n_dense: Optional[int] = None):
+        load()
+        self.tables = [_dev(t, torch.float32, "table") for t in tables]
+        self.bot_w = [_dev(w, torch.float32, "bot_w") for w in bot_w]
+        self.bot_b = [_dev(b, torch.float32, "bot_b") for b in bot_b]
+        self.top_w = [_dev(w, torch.float32, "top_w") for w in top_w]
+        self.top_b = [_dev(b, torch.float32, "top_b") for b in top_b]
+        self.device = self.tables[0].device
+        n0 = n_dense if n_dense is not None else self.bot_w[0].shape[1]
+        self.ln_bot = [int(n0)] + [int(w.shape[0]) for w in self.bot_w]
+        self.ln_top = [int(self.top_w[0].shape[1])] + [int(w.shape[0]) for w in self.top_w]
+        self.num_tables = len(self.tables)
+        self.dim = int(self.tables[0].shape[1])
+        self._keep = (_i64s(self.ln_bot), _i64s(self.ln_top), _i64s([t.shape[0] for t in self.tables]),
+                      _ptrs(self.tables), _ptrs(self.bot_w), _ptrs(self.bot_b), _ptrs(self.top_w), _ptrs(self.top_b))
+        lb, lt, rows, emb, bw, bb, tw, tb = self._keep
+        self._desc = _Model(len(self.ln_bot), ctypes.cast(lb, _i64p), len(self.ln_top), ctypes.cast(lt, _i64p),
+                            self.num_tables, self.dim, ctypes.cast(rows, _i64p), emb, bw, bb, tw, tb)
+        self._ws: Optional[torch.Tensor] = None
+
+    @classmethod
+    def from_inputs(cls, inp) -> "Model":
+        return cls(inp.tables, inp.bot_w, inp.bot_b, inp.top_w, inp.top_b, n_dense=inp.workload.n_dense)
+
+    def workspace_bytes(self, batch: int) -> int:
+        n = load().dlrm_forward_workspace_bytes(ctypes.byref(self._desc), int(batch))
+        if n == 0:
+            raise DlrmError(DLRM_E_SHAPE, "dlrm_forward_workspace_bytes", "invalid model or batch")
+        return int(n)
+
+    def workspace(self, batch: int) -> torch.Tensor:
+        need = self.workspace_bytes(batch)
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = torch.empty(need, dtype=torch.uint8, device=self.device)
+        return self._ws
+
+    def forward_args(self, dense, indices, offsets):
+        """Marshal the per-call pointer arrays once (reusable across calls on the same tensors)."""
+        B = dense.shape[0]
+        return (B, dense.data_ptr(), _ptrs(indices), _i64s([i.numel() for i in indices]), _ptrs(offsets))
+
+    def forward(self, dense: torch.Tensor, indices: List[torch.Tensor], offsets: List[torch.Tensor],
+                out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                args=None) -> torch.Tensor:
+        L = load()
+        _dev(dense, torch.float32, "dense")
+        if len(indices) != self.num_tables or len(offsets) != self.num_tables:
+            raise ValueError("one index and one offset tensor per table")
+        for t in range(self.num_tables):
+            _dev(indices[t], torch.int64, f"indices[{t}]")
+            _dev(offsets[t], torch.int64, f"offsets[{t}]")
+        B = dense.shape[0]
+        if dense.shape[1] != self.ln_bot[0] or any(o.shape[0] != B for o in offsets):
+            raise ValueError("shape mismatch")
+        if out is None:
+            out = torch.empty((B,), device=self.device, dtype=torch.float32)
+        _dev(out, torch.float32, "out")
+        if out.numel() != B:
+            raise ValueError("out must hold B values")
+        ws = workspace if workspace is not None else self.workspace(B)
+        if args is None:
+            args = self.forward_args(dense, indices, offsets)
+        b, dp, ip, nn_, op = args
+        rc = L.dlrm_forward(ctypes.byref(self._desc), b, dp, ip, nn_, op, out.data_ptr(), ws.data_ptr(),
+                            ws.numel() * ws.element_size(), _stream(self.device))
+        _check(rc, "dlrm_forward")
+        return out
+
+
+def check_indices(tables_rows: Sequence[int], indices: List[torch.Tensor], offsets: List[torch.Tensor]) -> int:
+    """Count malformed indices / offsets on the device (synchronises to read the count)."""
+    L = load()
+    T = len(indices)
+    dev = indices[0].device
+    bad = torch.empty(1, dtype=torch.int32, device=dev)
+    B = offsets[0].shape[0]
+    rc = L.dlrm_embbag_check_indices(T, B, _i64s(tables_rows), _ptrs(indices), _i64s([i.numel() for i in indices]),
+                                     _ptrs(offsets), bad.data_ptr(), _stream(dev))
+    _check(rc, "dlrm_embbag_check_indices")
+    return int(bad.item())
+
+
+def pair_index_map(n_feat: int, device="cuda"):
+    """The interaction kernels' own decoding p -> (i, j), as two int32 tensors."""
+    L = load()
+    P = n_pairs(n_feat)
+    i = torch.empty(max(P, 1), dtype=torch.int32, device=device)
+    j = torch.empty(max(P, 1), dtype=torch.int32, device=device)
+    rc = L.dlrm_pair_index_map(int(n_feat), i.data_ptr(), j.data_ptr(), _stream(i.device))
+    _check(rc, "dlrm_pair_index_map")
+    return i[:P], j[:P]

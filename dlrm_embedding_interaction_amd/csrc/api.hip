@@ -1,0 +1,264 @@
+// api.hip -- extern "C" entry points of the DLRMv1 forward library
+// (declared in include/dlrm_mi355x.h).  Host code only: argument validation,
+// workspace planning and kernel launches on the caller's stream.  Nothing here
+// allocates, copies or synchronises, so every call can be captured in a graph.
+#include <stdint.h>
+#include <string.h>
+
+#include "dlrm_internal.h"
+
+#define DLRM_API extern "C" __attribute__((visibility("default")))
+
+using namespace dlrm;
+
+namespace {
+
+inline bool al16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+inline int64_t round_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
+inline dlrm_status_t from_hip(hipError_t e) { return e == hipSuccess ? DLRM_OK : DLRM_E_HIP; }
+inline int64_t n_pairs(int64_t f) { return f * (f - 1) / 2; }
+
+constexpr int64_t kIntLimit = (int64_t)1 << 30;  // sizes kept well inside int for kernel indexing
+
+// Per-table bag arguments shared by the bag entry points and the forward.
+dlrm_status_t fill_tables(TableArgs& ta, int32_t T, int64_t B, int32_t D, const float* const* weights,
+                          const int64_t* rows, const int64_t* const* indices, const int64_t* n_indices,
+                          const int64_t* const* offsets, bool* aligned, bool* multi_hot) {
+    memset(&ta, 0, sizeof(ta));
+    bool al = (D % 4 == 0);
+    bool mh = false;
+    for (int32_t t = 0; t < T; ++t) {
+        if (!weights[t] || !offsets[t]) return DLRM_E_NULL;
+        if (rows[t] < 1 || n_indices[t] < 0 || n_indices[t] > kIntLimit * 64) return DLRM_E_SHAPE;
+        if (n_indices[t] > 0 && !indices[t]) return DLRM_E_NULL;
+        ta.w[t] = weights[t];
+        ta.idx[t] = indices[t];
+        ta.off[t] = offsets[t];
+        ta.nidx[t] = n_indices[t];
+        al = al && al16(weights[t]);
+        mh = mh || (n_indices[t] > B);
+    }
+    *aligned = al;
+    *multi_hot = mh;
+    return DLRM_OK;
+}
+
+bool interaction_fits(int32_t T, int32_t D) { return interact_lds_bytes(T, D, 1) <= kMaxLdsBytes; }
+
+// Workspace plan of the forward: R = [x | Z] (B, ldR) and two hidden
+// buffers (B, ldH), each region 256-byte aligned.
+struct Plan {
+    int64_t P, wr, ldR, ldH;
+    size_t off_r, off_h0, off_h1, total;
+};
+
+dlrm_status_t validate_model(const dlrm_model_t* m, int64_t B) {
+    if (!m) return DLRM_E_NULL;
+    if (!m->ln_bot || !m->ln_top) return DLRM_E_NULL;
+    if (m->n_bot < 2 || m->n_top < 2 || B < 1 || m->num_tables < 1 || m->emb_dim < 1) return DLRM_E_SHAPE;
+    if (m->n_bot > DLRM_MAX_LAYERS || m->n_top > DLRM_MAX_LAYERS) return DLRM_E_UNSUPPORTED;
+    if (m->num_tables > DLRM_MAX_TABLES || m->emb_dim > kMaxDim) return DLRM_E_UNSUPPORTED;
+    for (int32_t l = 0; l < m->n_bot; ++l)
+        if (m->ln_bot[l] < 1 || m->ln_bot[l] > kIntLimit) return DLRM_E_SHAPE;
+    for (int32_t l = 0; l < m->n_top; ++l)
+        if (m->ln_top[l] < 1 || m->ln_top[l] > kIntLimit) return DLRM_E_SHAPE;
+    if (m->ln_bot[m->n_bot - 1] != m->emb_dim) return DLRM_E_SHAPE;
+    if (m->ln_top[0] != m->emb_dim + n_pairs(m->num_tables + 1)) return DLRM_E_SHAPE;
+    if (m->ln_top[m->n_top - 1] != 1) return DLRM_E_SHAPE;
+    if (B > kIntLimit) return DLRM_E_UNSUPPORTED;
+    if (!interaction_fits(m->num_tables, m->emb_dim)) return DLRM_E_UNSUPPORTED;
+    return DLRM_OK;
+}
+
+void make_plan(const dlrm_model_t* m, int64_t B, Plan* p) {
+    p->P = n_pairs(m->num_tables + 1);
+    p->wr = m->emb_dim + p->P;
+    p->ldR = round_up(p->wr, 4);
+    int64_t maxh = 0;
+    for (int32_t l = 1; l + 1 < m->n_bot; ++l) maxh = maxh > m->ln_bot[l] ? maxh : m->ln_bot[l];
+    for (int32_t l = 1; l + 1 < m->n_top; ++l) maxh = maxh > m->ln_top[l] ? maxh : m->ln_top[l];
+    p->ldH = round_up(maxh, 4);
+    const size_t r_bytes = (size_t)round_up(B * p->ldR * (int64_t)sizeof(float), 256);
+    const size_t h_bytes = (size_t)round_up(B * p->ldH * (int64_t)sizeof(float), 256);
+    p->off_r = 0;
+    p->off_h0 = r_bytes;
+    p->off_h1 = r_bytes + h_bytes;
+    p->total = r_bytes + 2 * h_bytes;
+}
+
+}  // namespace
+
+DLRM_API const char* dlrm_status_string(dlrm_status_t s) {
+    switch (s) {
+        case DLRM_OK: return "DLRM_OK";
+        case DLRM_E_NULL: return "DLRM_E_NULL: a required pointer is NULL";
+        case DLRM_E_SHAPE: return "DLRM_E_SHAPE: inconsistent or non-positive sizes";
+        case DLRM_E_WORKSPACE: return "DLRM_E_WORKSPACE: workspace missing, misaligned or too small";
+        case DLRM_E_UNSUPPORTED: return "DLRM_E_UNSUPPORTED: sizes beyond the library's limits";
+        case DLRM_E_HIP: return "DLRM_E_HIP: a HIP launch failed";
+        case DLRM_E_INDEX: return "DLRM_E_INDEX: bag indices or offsets out of range";
+    }
+    return "unknown dlrm_status_t";
+}
+
+DLRM_API int32_t dlrm_abi_version(void) { return DLRM_ABI_VERSION; }
+
+DLRM_API dlrm_status_t dlrm_embbag_sum(int32_t num_tables, int64_t batch, int32_t dim, const float* const* weights,
+                                       const int64_t* rows, const int64_t* const* indices,
+                                       const int64_t* n_indices, const int64_t* const* offsets, float* out,
+                                       void* stream) {
+    if (!weights || !rows || !indices || !n_indices || !offsets || !out) return DLRM_E_NULL;
+    if (num_tables < 1 || batch < 1 || dim < 1) return DLRM_E_SHAPE;
+    if (num_tables > DLRM_MAX_TABLES || dim > kMaxDim || batch > kIntLimit) return DLRM_E_UNSUPPORTED;
+    TableArgs ta;
+    bool aligned, multi_hot;
+    dlrm_status_t st = fill_tables(ta, num_tables, batch, dim, weights, rows, indices, n_indices, offsets, &aligned,
+                                   &multi_hot);
+    if (st != DLRM_OK) return st;
+    aligned = aligned && al16(out);
+    return from_hip(launch_embbag_sum(ta, num_tables, dim, batch, aligned, multi_hot, out, (hipStream_t)stream));
+}
+
+DLRM_API dlrm_status_t dlrm_interact_lower_tri(int64_t batch, int32_t num_tables, int32_t dim, const float* x,
+                                               int64_t ld_x, const float* emb, float* out, int64_t ld_out,
+                                               int32_t concat_dense, void* stream) {
+    if (!x || !emb || !out) return DLRM_E_NULL;
+    if (batch < 1 || num_tables < 1 || dim < 1 || ld_x < dim) return DLRM_E_SHAPE;
+    if (num_tables > DLRM_MAX_TABLES || dim > kMaxDim || batch > kIntLimit) return DLRM_E_UNSUPPORTED;
+    if (!interaction_fits(num_tables, dim)) return DLRM_E_UNSUPPORTED;
+    const int64_t P = n_pairs(num_tables + 1);
+    if (ld_out < (concat_dense ? dim + P : P)) return DLRM_E_SHAPE;
+    const bool aligned = (dim % 4 == 0) && (ld_x % 4 == 0) && al16(x) && al16(emb);
+    return from_hip(launch_interact(nullptr, emb, num_tables, dim, batch, aligned, false, x, ld_x, out, ld_out,
+                                    concat_dense ? 0 : -1, concat_dense ? dim : 0, (hipStream_t)stream));
+}
+
+DLRM_API dlrm_status_t dlrm_embbag_interact(int32_t num_tables, int64_t batch, int32_t dim,
+                                            const float* const* weights, const int64_t* rows,
+                                            const int64_t* const* indices, const int64_t* n_indices,
+                                            const int64_t* const* offsets, const float* x, int64_t ld_x, float* out,
+                                            int64_t ld_out, int32_t concat_dense, void* stream) {
+    if (!weights || !rows || !indices || !n_indices || !offsets || !x || !out) return DLRM_E_NULL;
+    if (num_tables < 1 || batch < 1 || dim < 1 || ld_x < dim) return DLRM_E_SHAPE;
+    if (num_tables > DLRM_MAX_TABLES || dim > kMaxDim || batch > kIntLimit) return DLRM_E_UNSUPPORTED;
+    if (!interaction_fits(num_tables, dim)) return DLRM_E_UNSUPPORTED;
+    const int64_t P = n_pairs(num_tables + 1);
+    if (ld_out < (concat_dense ? dim + P : P)) return DLRM_E_SHAPE;
+    TableArgs ta;
+    bool aligned, multi_hot;
+    dlrm_status_t st = fill_tables(ta, num_tables, batch, dim, weights, rows, indices, n_indices, offsets, &aligned,
+                                   &multi_hot);
+    if (st != DLRM_OK) return st;
+    aligned = aligned && (ld_x % 4 == 0) && al16(x);
+    return from_hip(launch_interact(&ta, nullptr, num_tables, dim, batch, aligned, multi_hot, x, ld_x, out, ld_out,
+                                    concat_dense ? 0 : -1, concat_dense ? dim : 0, (hipStream_t)stream));
+}
+
+DLRM_API dlrm_status_t dlrm_linear_bias_act(int64_t M, int64_t N, int64_t K, const float* x, int64_t ld_x,
+                                            const float* W, const float* bias, int32_t act, float* y, int64_t ld_y,
+                                            void* stream) {
+    if (!x || !W || !y) return DLRM_E_NULL;
+    if (M < 1 || N < 1 || K < 1 || ld_x < K || ld_y < N) return DLRM_E_SHAPE;
+    if (act < DLRM_ACT_NONE || act > DLRM_ACT_SIGMOID) return DLRM_E_SHAPE;
+    if (M > kIntLimit || N > kIntLimit || K > kIntLimit) return DLRM_E_UNSUPPORTED;
+    return from_hip(launch_linear(M, N, K, x, ld_x, W, bias, act, y, ld_y, (hipStream_t)stream));
+}
+
+DLRM_API size_t dlrm_forward_workspace_bytes(const dlrm_model_t* m, int64_t batch) {
+    if (validate_model(m, batch) != DLRM_OK) return 0;
+    Plan p;
+    make_plan(m, batch, &p);
+    return p.total;
+}
+
+DLRM_API dlrm_status_t dlrm_forward(const dlrm_model_t* m, int64_t batch, const float* dense,
+                                    const int64_t* const* indices, const int64_t* n_indices,
+                                    const int64_t* const* offsets, float* out, void* workspace, size_t ws_bytes,
+                                    void* stream) {
+    dlrm_status_t st = validate_model(m, batch);
+    if (st != DLRM_OK) return st;
+    if (!dense || !indices || !n_indices || !offsets || !out) return DLRM_E_NULL;
+    if (!m->rows || !m->emb_w || !m->bot_w || !m->bot_b || !m->top_w || !m->top_b) return DLRM_E_NULL;
+    for (int32_t l = 0; l + 1 < m->n_bot; ++l)
+        if (!m->bot_w[l] || !m->bot_b[l]) return DLRM_E_NULL;
+    for (int32_t l = 0; l + 1 < m->n_top; ++l)
+        if (!m->top_w[l] || !m->top_b[l]) return DLRM_E_NULL;
+    const int32_t T = m->num_tables, D = m->emb_dim;
+    TableArgs ta;
+    bool aligned, multi_hot;
+    st = fill_tables(ta, T, batch, D, m->emb_w, m->rows, indices, n_indices, offsets, &aligned, &multi_hot);
+    if (st != DLRM_OK) return st;
+    Plan p;
+    make_plan(m, batch, &p);
+    if (!workspace || ((uintptr_t)workspace & 255u) != 0 || ws_bytes < p.total) return DLRM_E_WORKSPACE;
+
+    hipStream_t s = (hipStream_t)stream;
+    char* ws = (char*)workspace;
+    float* R = (float*)(ws + p.off_r);
+    float* H[2] = {(float*)(ws + p.off_h0), (float*)(ws + p.off_h1)};
+    int hsel = 0;
+
+    // 1. bottom MLP, ReLU after every layer; the last layer writes x into R[:, 0:D]
+    const float* in = dense;
+    int64_t ld_in = m->ln_bot[0];
+    for (int32_t l = 0; l + 1 < m->n_bot; ++l) {
+        const bool last = (l + 2 == m->n_bot);
+        float* o = last ? R : H[hsel];
+        const int64_t ld_o = last ? p.ldR : p.ldH;
+        hipError_t e = launch_linear(batch, m->ln_bot[l + 1], m->ln_bot[l], in, ld_in, m->bot_w[l], m->bot_b[l],
+                                     DLRM_ACT_RELU, o, ld_o, s);
+        if (e != hipSuccess) return DLRM_E_HIP;
+        if (!last) hsel ^= 1;
+        in = o;
+        ld_in = ld_o;
+    }
+
+    // 2-5. bags gathered into LDS, dots, Z written into R[:, D:D+P]
+    {
+        hipError_t e = launch_interact(&ta, nullptr, T, D, batch, aligned, multi_hot, R, p.ldR, R, p.ldR, -1, D, s);
+        if (e != hipSuccess) return DLRM_E_HIP;
+    }
+
+    // 6-7. top MLP: ReLU on hidden layers, sigmoid on the one-output last layer
+    in = R;
+    ld_in = p.ldR;
+    for (int32_t l = 0; l + 1 < m->n_top; ++l) {
+        const bool last = (l + 2 == m->n_top);
+        float* o = last ? out : H[hsel];
+        const int64_t ld_o = last ? 1 : p.ldH;
+        hipError_t e = launch_linear(batch, m->ln_top[l + 1], m->ln_top[l], in, ld_in, m->top_w[l], m->top_b[l],
+                                     last ? DLRM_ACT_SIGMOID : DLRM_ACT_RELU, o, ld_o, s);
+        if (e != hipSuccess) return DLRM_E_HIP;
+        if (!last) hsel ^= 1;
+        in = o;
+        ld_in = ld_o;
+    }
+    return DLRM_OK;
+}
+
+DLRM_API dlrm_status_t dlrm_embbag_check_indices(int32_t num_tables, int64_t batch, const int64_t* rows,
+                                                 const int64_t* const* indices, const int64_t* n_indices,
+                                                 const int64_t* const* offsets, int32_t* bad_count_device,
+                                                 void* stream) {
+    if (!rows || !indices || !n_indices || !offsets || !bad_count_device) return DLRM_E_NULL;
+    if (num_tables < 1 || batch < 1) return DLRM_E_SHAPE;
+    if (num_tables > DLRM_MAX_TABLES) return DLRM_E_UNSUPPORTED;
+    CheckArgs ca;
+    memset(&ca, 0, sizeof(ca));
+    for (int32_t t = 0; t < num_tables; ++t) {
+        if (!offsets[t]) return DLRM_E_NULL;
+        if (n_indices[t] < 0) return DLRM_E_SHAPE;
+        if (n_indices[t] > 0 && !indices[t]) return DLRM_E_NULL;
+        ca.idx[t] = indices[t];
+        ca.off[t] = offsets[t];
+        ca.nidx[t] = n_indices[t];
+        ca.rows[t] = rows[t];
+    }
+    return from_hip(launch_check_indices(ca, num_tables, batch, bad_count_device, (hipStream_t)stream));
+}
+
+DLRM_API dlrm_status_t dlrm_pair_index_map(int32_t n_feat, int32_t* i_out, int32_t* j_out, void* stream) {
+    if (!i_out || !j_out) return DLRM_E_NULL;
+    if (n_feat < 2 || n_feat > 4096) return DLRM_E_SHAPE;
+    return from_hip(launch_pair_index_map(n_feat, i_out, j_out, (hipStream_t)stream));
+}

@@ -1,0 +1,50 @@
+// dlrm_internal.h -- host-side launch functions shared between the kernel
+// sources and the C-ABI entry points of the DLRMv1 forward library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "dlrm_device.h"
+
+namespace dlrm {
+
+constexpr int kMaxDim = 1024;                       // longest embedding row supported
+constexpr size_t kInteractLdsBudget = 32 * 1024;     // target LDS per interaction block
+constexpr size_t kMaxLdsBytes = 64 * 1024;           // hard LDS limit per block
+
+// Arguments of the device-side bag-data check.
+struct CheckArgs {
+    const int64_t* idx[DLRM_MAX_TABLES];
+    const int64_t* off[DLRM_MAX_TABLES];
+    int64_t nidx[DLRM_MAX_TABLES];
+    int64_t rows[DLRM_MAX_TABLES];
+};
+
+bool row_shape_supported(int D);
+int interact_samples_per_block(int T, int D, int64_t B);
+size_t interact_lds_bytes(int T, int D, int spb);
+
+// Bags of T tables into out (B, T, D).  aligned16: every table row and the
+// output allow 16-byte access.  multi_hot: bags hold more than one index on
+// average (selects deeper per-bag prefetch).
+hipError_t launch_embbag_sum(const TableArgs& ta, int T, int D, int64_t B, bool aligned16, bool multi_hot,
+                             float* out, hipStream_t s);
+
+// Interaction over [x, E_0..E_{T-1}] writing Z to out[:, col_z:col_z+P] and,
+// when col_x >= 0, x to out[:, col_x:col_x+D].  With ta != NULL the E rows
+// are gathered from the tables (fused path); otherwise read from emb (B, T, D).
+hipError_t launch_interact(const TableArgs* ta, const float* emb, int T, int D, int64_t B, bool aligned16,
+                           bool multi_hot, const float* x, int64_t ld_x, float* out, int64_t ld_out, int col_x,
+                           int col_z, hipStream_t s);
+
+hipError_t launch_check_indices(const CheckArgs& ca, int T, int64_t B, int32_t* bad, hipStream_t s);
+
+hipError_t launch_pair_index_map(int F, int32_t* i_out, int32_t* j_out, hipStream_t s);
+
+// y = act(x W^T + bias): MFMA for N > 1, a dot-product kernel for N == 1.
+hipError_t launch_linear(int64_t M, int64_t N, int64_t K, const float* x, int64_t ld_x, const float* W,
+                         const float* bias, int act, float* y, int64_t ld_y, hipStream_t s);
+
+}  // namespace dlrm

@@ -1,0 +1,418 @@
+// embbag_interact.hip -- gfx950 kernels for the sparse half of the DLRMv1
+// forward: multi-table sum-pooled embedding bags, the strict-lower-triangle
+// pairwise-dot interaction, and the two fused (bags gathered straight into LDS,
+// then dotted there).
+//
+// Definitions:
+//  * bag sum: out[b][t] = sum of rows idx_t[k], k in [off_t[b], end_t(b)),
+//    end_t(b) = off_t[b+1] or the index count for the last bag (LessonsLearned
+//    "DLRM compile: EmbeddingBag translator gap" point 2 and movement.rs
+//    translate_embedding_bag, on "luminal compare dlrm-fused-kernels...
+//    dlrm-pt2-megakernel");
+//  * interaction: Z[b][p] = <S_b[i], S_b[j]>, p = i(i-1)/2 + j, j < i < F,
+//    S_b = [x_b, E_b0, ..., E_b(T-1)] (dlrm_megakernel.rs cuda_source step 4
+//    on the same page; PairwiseDotLowerTriStackedKernel on "luminal compare
+//    asglover/modal_ci_ready...vanilla-pytorch", cuda_lite kernels).
+//
+// Design on CDNA4 (not the pages' CUDA layouts):
+//  * one embedding row is read by a group of G lanes, 16 bytes per lane
+//    (global_load_dwordx4), so a wave64 reads 1 KiB per instruction; each
+//    group keeps U bags in flight and prefetches R row indices per bag, so a
+//    wave has U*R independent row loads outstanding;
+//  * the fused kernel places the F vectors of each of its samples in LDS,
+//    then every G-lane group takes one flat pair index p at a time, decodes
+//    (i, j) in closed form, dots the two LDS rows and reduces across the group
+//    with DPP / ds_swizzle; the P results of a sample are staged in LDS and
+//    written as one contiguous row segment.
+#include "dlrm_device.h"
+#include "dlrm_internal.h"
+
+namespace dlrm {
+
+template <int VEC> struct Vec;
+template <> struct Vec<4> {
+    using T = float4;
+    static __device__ __forceinline__ T zero() { return make_float4(0.f, 0.f, 0.f, 0.f); }
+    static __device__ __forceinline__ T load(const float* p) { return *reinterpret_cast<const float4*>(p); }
+    static __device__ __forceinline__ void store(float* p, T v) { *reinterpret_cast<float4*>(p) = v; }
+    static __device__ __forceinline__ T add(T a, T b) { return f4_add(a, b); }
+    static __device__ __forceinline__ float dot(T a, T b, float acc) { return f4_dot(a, b, acc); }
+};
+template <> struct Vec<1> {
+    using T = float;
+    static __device__ __forceinline__ T zero() { return 0.f; }
+    static __device__ __forceinline__ T load(const float* p) { return *p; }
+    static __device__ __forceinline__ void store(float* p, T v) { *p = v; }
+    static __device__ __forceinline__ T add(T a, T b) { return a + b; }
+    static __device__ __forceinline__ float dot(T a, T b, float acc) { return fmaf(a, b, acc); }
+};
+
+// Sum U bags per lane group.  Bag q[u] (-1 = none) is local bag number
+// q = sl * T + t of sample b_base + sl.  Lane lg of the group owns elements
+// (c * G + lg) * VEC .. + VEC-1 of the row for c < C.  Rows of one bag are
+// added in increasing k, R of them fetched per step.
+template <int VEC, int G, int C, int U, int R>
+__device__ __forceinline__ void gather_bags(const TableArgs& ta, int T, int D, int64_t B, int64_t b_base,
+                                            const int (&q)[U], int lg,
+                                            typename Vec<VEC>::T (&acc)[U][C]) {
+    using V = Vec<VEC>;
+    const float* wp[U];
+    const int64_t* ip[U];
+    int len[U];
+    int maxlen = 0;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        len[u] = 0;
+        wp[u] = nullptr;
+        ip[u] = nullptr;
+        if (q[u] >= 0) {
+            const int sl = q[u] / T;
+            const int t = q[u] - sl * T;
+            const int64_t b = b_base + sl;
+            const int64_t* off = ta.off[t];
+            const int64_t s = off[b];
+            const int64_t e = (b + 1 < B) ? off[b + 1] : ta.nidx[t];
+            len[u] = (int)(e - s);
+            wp[u] = ta.w[t];
+            ip[u] = ta.idx[t] + s;
+        }
+        maxlen = max(maxlen, len[u]);
+#pragma unroll
+        for (int c = 0; c < C; ++c) acc[u][c] = V::zero();
+    }
+    for (int r0 = 0; r0 < maxlen; r0 += R) {
+        int64_t row[R][U];
+#pragma unroll
+        for (int rr = 0; rr < R; ++rr)
+#pragma unroll
+            for (int u = 0; u < U; ++u) row[rr][u] = (r0 + rr < len[u]) ? ip[u][r0 + rr] : -1;
+        typename V::T v[R][U][C];
+#pragma unroll
+        for (int rr = 0; rr < R; ++rr)
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int c = 0; c < C; ++c) {
+                    const int e = (c * G + lg) * VEC;
+                    v[rr][u][c] = (row[rr][u] >= 0 && e < D) ? V::load(wp[u] + row[rr][u] * D + e) : V::zero();
+                }
+#pragma unroll
+        for (int rr = 0; rr < R; ++rr)
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (row[rr][u] >= 0) {
+#pragma unroll
+                    for (int c = 0; c < C; ++c) acc[u][c] = V::add(acc[u][c], v[rr][u][c]);
+                }
+    }
+}
+
+// ---- standalone multi-table bags: out (B, T, D) -------------------------------
+template <int VEC, int G, int C, int U, int R>
+__global__ __launch_bounds__(kBlock) void embbag_sum_kernel(TableArgs ta, int T, int D, int64_t B, float* out) {
+    using V = Vec<VEC>;
+    constexpr int NG = kBlock / G;
+    const int lg = threadIdx.x % G;
+    const int g = threadIdx.x / G;
+    const int64_t nbags = B * T;
+    const int64_t base = (int64_t)blockIdx.x * NG * U;
+    // Local bag numbers relative to sample base_b = base / T keep int range.
+    const int64_t b_base = base / T;
+    const int64_t q_off = b_base * T;
+    int q[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t qq = base + u * NG + g;
+        q[u] = (qq < nbags) ? (int)(qq - q_off) : -1;
+    }
+    typename V::T acc[U][C];
+    gather_bags<VEC, G, C, U, R>(ta, T, D, B, b_base, q, lg, acc);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        if (q[u] < 0) continue;
+        float* o = out + (q_off + q[u]) * (int64_t)D;
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            const int e = (c * G + lg) * VEC;
+            if (e < D) V::store(o + e, acc[u][c]);
+        }
+    }
+}
+
+// ---- interaction, with the bags either gathered (GATHER) or read from E ------
+// LDS: S[spb][F][D] then Zs[spb][P].
+template <int VEC, int G, int C, int U, int R, bool GATHER>
+__global__ __launch_bounds__(kBlock) void interact_kernel(TableArgs ta, const float* __restrict__ emb, int T,
+                                                          int D, int64_t B, int spb, const float* x,
+                                                          int64_t ld_x, float* out, int64_t ld_out,
+                                                          int col_x, int col_z) {
+    using V = Vec<VEC>;
+    constexpr int NG = kBlock / G;
+    extern __shared__ float4 lds4[];
+    float* S = reinterpret_cast<float*>(lds4);
+    const int F = T + 1;
+    const int P = F * (F - 1) / 2;
+    float* Zs = S + (size_t)spb * F * D;
+    const int tid = threadIdx.x;
+    const int lg = tid % G;
+    const int g = tid / G;
+    const int64_t b0 = (int64_t)blockIdx.x * spb;
+    const int nb = (int)min((int64_t)spb, B - b0);
+    const int dv = D / VEC;
+
+    // 1. x rows into S[s][0]
+    for (int e = tid; e < nb * dv; e += kBlock) {
+        const int s = e / dv;
+        const int d = (e - s * dv) * VEC;
+        V::store(S + (size_t)s * F * D + d, V::load(x + (b0 + s) * ld_x + d));
+    }
+    // 2. table vectors into S[s][1 + t]
+    if constexpr (GATHER) {
+        const int nbag = nb * T;
+        for (int qb = 0; qb < nbag; qb += NG * U) {
+            int q[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int qq = qb + u * NG + g;
+                q[u] = qq < nbag ? qq : -1;
+            }
+            typename V::T acc[U][C];
+            gather_bags<VEC, G, C, U, R>(ta, T, D, B, b0, q, lg, acc);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (q[u] < 0) continue;
+                const int s = q[u] / T;
+                const int t = q[u] - s * T;
+                float* dst = S + ((size_t)s * F + 1 + t) * D;
+#pragma unroll
+                for (int c = 0; c < C; ++c) {
+                    const int e = (c * G + lg) * VEC;
+                    if (e < D) V::store(dst + e, acc[u][c]);
+                }
+            }
+        }
+    } else {
+        const int per = T * dv;
+        for (int e = tid; e < nb * per; e += kBlock) {
+            const int s = e / per;
+            const int r = e - s * per;  // element (in VEC units) within the (T, D) block
+            const int t = r / dv;
+            const int d = (r - t * dv) * VEC;
+            V::store(S + ((size_t)s * F + 1 + t) * D + d, V::load(emb + ((b0 + s) * T + t) * (int64_t)D + d));
+        }
+    }
+    __syncthreads();
+
+    // 3. dots: one flat pair index per lane group at a time
+    const int npairs = nb * P;
+    for (int w = g; w < npairs; w += NG) {
+        const int s = w / P;
+        const int p = w - s * P;
+        int i, j;
+        pair_from_flat(p, i, j);
+        const float* si = S + ((size_t)s * F + i) * D;
+        const float* sj = S + ((size_t)s * F + j) * D;
+        float part = 0.f;
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            const int e = (c * G + lg) * VEC;
+            if (e < D) part = V::dot(V::load(si + e), V::load(sj + e), part);
+        }
+        const float tot = group_sum<G>(part);
+        if (lg == 0) Zs[w] = tot;
+    }
+    __syncthreads();
+
+    // 4. write Z (and x) rows
+    for (int e = tid; e < npairs; e += kBlock) {
+        const int s = e / P;
+        const int p = e - s * P;
+        out[(b0 + s) * ld_out + col_z + p] = Zs[e];
+    }
+    if (col_x >= 0) {
+        for (int e = tid; e < nb * D; e += kBlock) {
+            const int s = e / D;
+            const int d = e - s * D;
+            out[(b0 + s) * ld_out + col_x + d] = S[(size_t)s * F * D + d];
+        }
+    }
+}
+
+// ---- device-side validation of bag data ------------------------------------------
+__global__ void zero_i32_kernel(int32_t* p) { *p = 0; }
+
+__global__ __launch_bounds__(kBlock) void check_indices_kernel(CheckArgs ca, int T, int64_t B, int32_t* bad) {
+    int64_t local = 0;
+    const int64_t stride = (int64_t)gridDim.x * kBlock;
+    for (int t = 0; t < T; ++t) {
+        const int64_t rows = ca.rows[t];
+        const int64_t n = ca.nidx[t];
+        for (int64_t k = (int64_t)blockIdx.x * kBlock + threadIdx.x; k < n; k += stride) {
+            const int64_t v = ca.idx[t][k];
+            local += (v < 0 || v >= rows);
+        }
+        for (int64_t b = (int64_t)blockIdx.x * kBlock + threadIdx.x; b < B; b += stride) {
+            const int64_t s = ca.off[t][b];
+            const int64_t e = (b + 1 < B) ? ca.off[t][b + 1] : n;
+            local += (s < 0 || s > e || e > n);
+        }
+    }
+    if (local) atomicAdd(bad, (int32_t)min(local, (int64_t)1 << 30));
+}
+
+// ---- the kernels' own pair-index decoding, exported for tests -----------------
+__global__ __launch_bounds__(kBlock) void pair_map_kernel(int P, int32_t* io, int32_t* jo) {
+    const int p = blockIdx.x * kBlock + threadIdx.x;
+    if (p >= P) return;
+    int i, j;
+    pair_from_flat(p, i, j);
+    io[p] = i;
+    jo[p] = j;
+}
+
+// ---- host-side dispatch ---------------------------------------------------------
+
+static int pow2_at_least(int v) {
+    int p = 1;
+    while (p < v) p <<= 1;
+    return p;
+}
+
+// Picks VEC, G, C for row length D and whether 16-byte access is allowed.
+struct RowShape {
+    int vec, g, c;
+};
+static RowShape row_shape(int D, bool aligned16) {
+    RowShape r;
+    r.vec = (aligned16 && D % 4 == 0) ? 4 : 1;
+    const int units = D / r.vec;
+    if (r.vec == 4) {
+        r.g = units <= 64 ? pow2_at_least(units) : 64;
+        r.c = (units + r.g - 1) / r.g;
+        r.c = pow2_at_least(r.c);
+    } else {
+        r.g = 64;
+        r.c = pow2_at_least((units + 63) / 64);
+    }
+    return r;
+}
+
+bool row_shape_supported(int D) { return D >= 1 && D <= kMaxDim; }
+
+template <int VEC, int G, int C, int U, int R>
+static hipError_t launch_embbag_t(const TableArgs& ta, int T, int D, int64_t B, float* out, hipStream_t s) {
+    constexpr int NG = kBlock / G;
+    const int64_t nbags = B * T;
+    const int64_t blocks = (nbags + (int64_t)NG * U - 1) / ((int64_t)NG * U);
+    hipLaunchKernelGGL((embbag_sum_kernel<VEC, G, C, U, R>), dim3((unsigned)blocks), dim3(kBlock), 0, s, ta, T, D, B,
+                       out);
+    return hipGetLastError();
+}
+
+template <int VEC, int G, int C, int U, int R, bool GATHER>
+static hipError_t launch_interact_t(const TableArgs& ta, const float* emb, int T, int D, int64_t B, int spb,
+                                    const float* x, int64_t ld_x, float* out, int64_t ld_out, int col_x, int col_z,
+                                    hipStream_t s) {
+    const int F = T + 1, P = F * (F - 1) / 2;
+    const size_t lds = sizeof(float) * ((size_t)spb * F * D + (size_t)spb * P);
+    const int64_t blocks = (B + spb - 1) / spb;
+    hipLaunchKernelGGL((interact_kernel<VEC, G, C, U, R, GATHER>), dim3((unsigned)blocks), dim3(kBlock), lds, s, ta,
+                       emb, T, D, B, spb, x, ld_x, out, ld_out, col_x, col_z);
+    return hipGetLastError();
+}
+
+// Dispatch over (VEC, G, C) with a functor template F<VEC, G, C>.
+#define DLRM_DISPATCH_ROW(rs, CALL)                                        \
+    do {                                                                   \
+        if ((rs).vec == 4) {                                               \
+            switch ((rs).g * 16 + ((rs).c > 1 ? (rs).c : 0)) {             \
+                case 1 * 16: { CALL(4, 1, 1); }                            \
+                case 2 * 16: { CALL(4, 2, 1); }                            \
+                case 4 * 16: { CALL(4, 4, 1); }                            \
+                case 8 * 16: { CALL(4, 8, 1); }                            \
+                case 16 * 16: { CALL(4, 16, 1); }                          \
+                case 32 * 16: { CALL(4, 32, 1); }                          \
+                case 64 * 16: { CALL(4, 64, 1); }                          \
+                case 64 * 16 + 2: { CALL(4, 64, 2); }                      \
+                case 64 * 16 + 4: { CALL(4, 64, 4); }                      \
+                default: return hipErrorInvalidValue;                      \
+            }                                                              \
+        } else {                                                           \
+            switch ((rs).c) {                                              \
+                case 1: { CALL(1, 64, 1); }                                \
+                case 2: { CALL(1, 64, 2); }                                \
+                case 4: { CALL(1, 64, 4); }                                \
+                case 8: { CALL(1, 64, 8); }                                \
+                case 16: { CALL(1, 64, 16); }                              \
+                default: return hipErrorInvalidValue;                      \
+            }                                                              \
+        }                                                                  \
+    } while (0)
+
+hipError_t launch_embbag_sum(const TableArgs& ta, int T, int D, int64_t B, bool aligned16, bool multi_hot,
+                             float* out, hipStream_t s) {
+    const RowShape rs = row_shape(D, aligned16);
+#define CALL_E(V, G, C)                                                            \
+    if (multi_hot) return launch_embbag_t<V, G, C, 4, 4>(ta, T, D, B, out, s);     \
+    return launch_embbag_t<V, G, C, 8, 1>(ta, T, D, B, out, s);
+    DLRM_DISPATCH_ROW(rs, CALL_E);
+#undef CALL_E
+}
+
+int interact_samples_per_block(int T, int D, int64_t B) {
+    const int F = T + 1, P = F * (F - 1) / 2;
+    const size_t per = sizeof(float) * ((size_t)F * D + P);
+    int spb = (int)(kInteractLdsBudget / per);
+    if (spb < 1) spb = 1;
+    if (spb > 16) spb = 16;
+    // keep at least ~2 blocks per CU when the batch allows it
+    const int64_t want = (B + 511) / 512;
+    if (want < spb) spb = (int)(want < 1 ? 1 : want);
+    return spb;
+}
+
+size_t interact_lds_bytes(int T, int D, int spb) {
+    const int F = T + 1, P = F * (F - 1) / 2;
+    return sizeof(float) * ((size_t)spb * F * D + (size_t)spb * P);
+}
+
+hipError_t launch_interact(const TableArgs* ta, const float* emb, int T, int D, int64_t B, bool aligned16,
+                           bool multi_hot, const float* x, int64_t ld_x, float* out, int64_t ld_out, int col_x,
+                           int col_z, hipStream_t s) {
+    const RowShape rs = row_shape(D, aligned16);
+    const int spb = interact_samples_per_block(T, D, B);
+    if (interact_lds_bytes(T, D, spb) > kMaxLdsBytes) return hipErrorInvalidValue;
+    TableArgs dummy{};
+    const TableArgs& t = ta ? *ta : dummy;
+    const bool gather = (ta != nullptr);
+#define CALL_I(V, G, C)                                                                                         \
+    if (!gather) return launch_interact_t<V, G, C, 1, 1, false>(t, emb, T, D, B, spb, x, ld_x, out, ld_out,     \
+                                                                col_x, col_z, s);                              \
+    if (multi_hot) return launch_interact_t<V, G, C, 4, 4, true>(t, emb, T, D, B, spb, x, ld_x, out, ld_out,   \
+                                                                 col_x, col_z, s);                             \
+    return launch_interact_t<V, G, C, 8, 1, true>(t, emb, T, D, B, spb, x, ld_x, out, ld_out, col_x, col_z, s);
+    DLRM_DISPATCH_ROW(rs, CALL_I);
+#undef CALL_I
+}
+
+hipError_t launch_pair_index_map(int F, int32_t* i_out, int32_t* j_out, hipStream_t s) {
+    const int P = F * (F - 1) / 2;
+    hipLaunchKernelGGL(pair_map_kernel, dim3((unsigned)((P + kBlock - 1) / kBlock)), dim3(kBlock), 0, s, P, i_out,
+                       j_out);
+    return hipGetLastError();
+}
+
+hipError_t launch_check_indices(const CheckArgs& ca, int T, int64_t B, int32_t* bad, hipStream_t s) {
+    hipLaunchKernelGGL(zero_i32_kernel, dim3(1), dim3(1), 0, s, bad);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    int64_t n = B;
+    for (int t = 0; t < T; ++t) n = n > ca.nidx[t] ? n : ca.nidx[t];
+    int64_t blocks = (n + kBlock - 1) / kBlock;
+    if (blocks > 4096) blocks = 4096;
+    if (blocks < 1) blocks = 1;
+    hipLaunchKernelGGL(check_indices_kernel, dim3((unsigned)blocks), dim3(kBlock), 0, s, ca, T, B, bad);
+    return hipGetLastError();
+}
+
+}  // namespace dlrm

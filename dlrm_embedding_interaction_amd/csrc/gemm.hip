@@ -1,0 +1,298 @@
+// gemm.hip -- fp32 Linear layers of the DLRMv1 MLPs on gfx950 matrix cores.
+//
+// y = act(x W^T + bias) with W in the nn.Linear (N, K) layout: the
+// addmm(bias, x, weight.t()) fast path with an absorbed ReLU / sigmoid
+// consumer (linear_bias, linear_bias_relu, linear_bias_sigmoid on "luminal
+// compare asglover/modal_ci_ready...vanilla-pytorch", Translator section;
+// sigmoid = 1/(1+exp(-a)) as KernelSigmoid on "luminal compare
+// nvidia-devcontainer-args...perf/compile-write-rayon").
+//
+// Both operands are K-contiguous ("NT"), so a tile of each is staged in LDS as
+// [row][k] with 4 floats of padding per row.  A wave owns a (TM*16) x (TN*16)
+// sub-tile built from v_mfma_f32_16x16x4f32 blocks; for every 16-wide k slice
+// each lane reads one float4 of A and one of B from LDS and feeds their
+// four components to four MFMAs (lane l supplies A[l%16][k] and B[k][l%16]
+// with k = 4*(l/16) + q for MFMA q, a permutation of the k order that both
+// operands share).  The next k tile is prefetched into registers while the
+// current one is multiplied.  Bias and activation are applied to the
+// accumulators before the single store.  Block order is remapped so that the
+// blocks one XCD runs (the hardware deals blocks to the 8 XCDs round-robin)
+// cover consecutive tiles and share their rows of x in that XCD's L2.
+#include "dlrm_device.h"
+#include "dlrm_internal.h"
+
+namespace dlrm {
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float apply_act(float v, int act) {
+    if (act == DLRM_ACT_RELU) return v > 0.f ? v : 0.f;
+    if (act == DLRM_ACT_SIGMOID) return 1.f / (1.f + expf(-v));
+    return v;
+}
+
+template <int BM, int BN, int BK, int WM, int WN, bool VA, bool VB>
+__global__ __launch_bounds__(WM* WN * 64) void gemm_bias_act_kernel(int M, int N, int K, const float* __restrict__ A,
+                                                                    int64_t lda, const float* __restrict__ W,
+                                                                    const float* __restrict__ bias, int act,
+                                                                    float* __restrict__ Y, int64_t ldy, int tiles_m,
+                                                                    int tiles_n) {
+    constexpr int NT = WM * WN * 64;
+    constexpr int TM = BM / (WM * 16);
+    constexpr int TN = BN / (WN * 16);
+    constexpr int LDK = BK + 4;
+    static_assert(BK % 16 == 0, "BK must be a multiple of 16");
+    static_assert(TM >= 1 && TN >= 1, "wave tile too small");
+    constexpr int A_V = VA ? (BM * BK / 4) / NT : (BM * BK) / NT;  // loads per thread
+    constexpr int B_V = VB ? (BN * BK / 4) / NT : (BN * BK) / NT;
+    static_assert(A_V >= 1 && B_V >= 1, "tile too small for the block");
+    static_assert((VA ? A_V * 4 : A_V) * NT == BM * BK, "A tile must split evenly");
+    static_assert((VB ? B_V * 4 : B_V) * NT == BN * BK, "B tile must split evenly");
+
+    __shared__ __attribute__((aligned(16))) float As[BM * LDK];
+    __shared__ __attribute__((aligned(16))) float Bs[BN * LDK];
+
+    const int nblk = tiles_m * tiles_n;
+    int bid = blockIdx.x;
+    if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
+    const int tmi = bid / tiles_n;
+    const int tni = bid - tmi * tiles_n;
+    const int m0 = tmi * BM;
+    const int n0 = tni * BN;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave / WN;
+    const int wn = wave - wm * WN;
+
+    floatx4 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    floatx4 ra4[VA ? A_V : 1];
+    float ra1[VA ? 1 : A_V];
+    floatx4 rb4[VB ? B_V : 1];
+    float rb1[VB ? 1 : B_V];
+
+    auto load_tiles = [&](int k0) {
+        if constexpr (VA) {
+#pragma unroll
+            for (int i = 0; i < A_V; ++i) {
+                const int f = i * NT + tid;
+                const int r = f / (BK / 4);
+                const int k = k0 + (f - r * (BK / 4)) * 4;
+                const int m = m0 + r;
+                floatx4 v = {0.f, 0.f, 0.f, 0.f};
+                if (m < M) {
+                    const float* p = A + (int64_t)m * lda + k;
+                    if (k + 3 < K) {
+                        v = *reinterpret_cast<const floatx4*>(p);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (k + e < K) v[e] = p[e];
+                    }
+                }
+                ra4[i] = v;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < A_V; ++i) {
+                const int f = i * NT + tid;
+                const int r = f / BK;
+                const int k = k0 + (f - r * BK);
+                const int m = m0 + r;
+                ra1[i] = (m < M && k < K) ? A[(int64_t)m * lda + k] : 0.f;
+            }
+        }
+        if constexpr (VB) {
+#pragma unroll
+            for (int i = 0; i < B_V; ++i) {
+                const int f = i * NT + tid;
+                const int r = f / (BK / 4);
+                const int k = k0 + (f - r * (BK / 4)) * 4;
+                const int n = n0 + r;
+                floatx4 v = {0.f, 0.f, 0.f, 0.f};
+                if (n < N) {
+                    const float* p = W + (int64_t)n * K + k;
+                    if (k + 3 < K) {
+                        v = *reinterpret_cast<const floatx4*>(p);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (k + e < K) v[e] = p[e];
+                    }
+                }
+                rb4[i] = v;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < B_V; ++i) {
+                const int f = i * NT + tid;
+                const int r = f / BK;
+                const int k = k0 + (f - r * BK);
+                const int n = n0 + r;
+                rb1[i] = (n < N && k < K) ? W[(int64_t)n * K + k] : 0.f;
+            }
+        }
+    };
+    auto store_tiles = [&]() {
+        if constexpr (VA) {
+#pragma unroll
+            for (int i = 0; i < A_V; ++i) {
+                const int f = i * NT + tid;
+                const int r = f / (BK / 4);
+                const int c = (f - r * (BK / 4)) * 4;
+                *reinterpret_cast<floatx4*>(&As[r * LDK + c]) = ra4[i];
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < A_V; ++i) {
+                const int f = i * NT + tid;
+                const int r = f / BK;
+                As[r * LDK + (f - r * BK)] = ra1[i];
+            }
+        }
+        if constexpr (VB) {
+#pragma unroll
+            for (int i = 0; i < B_V; ++i) {
+                const int f = i * NT + tid;
+                const int r = f / (BK / 4);
+                const int c = (f - r * (BK / 4)) * 4;
+                *reinterpret_cast<floatx4*>(&Bs[r * LDK + c]) = rb4[i];
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < B_V; ++i) {
+                const int f = i * NT + tid;
+                const int r = f / BK;
+                Bs[r * LDK + (f - r * BK)] = rb1[i];
+            }
+        }
+    };
+
+    const int lrow = lane & 15;
+    const int lk = (lane >> 4) * 4;
+    const int arow0 = wm * TM * 16 + lrow;
+    const int brow0 = wn * TN * 16 + lrow;
+
+    load_tiles(0);
+    for (int k0 = 0; k0 < K; k0 += BK) {
+        store_tiles();
+        __syncthreads();
+        if (k0 + BK < K) load_tiles(k0 + BK);
+#pragma unroll
+        for (int kk = 0; kk < BK; kk += 16) {
+            floatx4 af[TM], bf[TN];
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+                af[i] = *reinterpret_cast<const floatx4*>(&As[(arow0 + i * 16) * LDK + kk + lk]);
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                bf[j] = *reinterpret_cast<const floatx4*>(&Bs[(brow0 + j * 16) * LDK + kk + lk]);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+#pragma unroll
+                    for (int j = 0; j < TN; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[i][q], bf[j][q], acc[i][j], 0, 0, 0);
+        }
+        __syncthreads();
+    }
+
+    // Accumulator layout of the 16x16 block: lane l, element r holds
+    // row 4*(l/16) + r, column l%16.
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+        const int n = n0 + wn * TN * 16 + j * 16 + (lane & 15);
+        const float bv = (bias != nullptr && n < N) ? bias[n] : 0.f;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int m = m0 + wm * TM * 16 + i * 16 + (lane >> 4) * 4 + r;
+                if (m < M && n < N) Y[(int64_t)m * ldy + n] = apply_act(acc[i][j][r] + bv, act);
+            }
+        }
+    }
+}
+
+// One wave per row: y[m] = act(<x[m], w> + bias).
+template <bool VA>
+__global__ __launch_bounds__(256) void gemv_bias_act_kernel(int M, int K, const float* __restrict__ A, int64_t lda,
+                                                            const float* __restrict__ w,
+                                                            const float* __restrict__ bias, int act,
+                                                            float* __restrict__ y, int64_t ldy) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= M) return;  // uniform per wave
+    const float* a = A + row * lda;
+    float acc = 0.f;
+    if constexpr (VA) {
+        for (int k = lane * 4; k < K; k += 256) {
+            if (k + 3 < K) {
+                acc = f4_dot(*reinterpret_cast<const float4*>(a + k), *reinterpret_cast<const float4*>(w + k), acc);
+            } else {
+                for (int e = 0; e < 4; ++e)
+                    if (k + e < K) acc = fmaf(a[k + e], w[k + e], acc);
+            }
+        }
+    } else {
+        for (int k = lane; k < K; k += 64) acc = fmaf(a[k], w[k], acc);
+    }
+    acc = group_sum<64>(acc);
+    if (lane == 0) y[row * ldy] = apply_act(acc + (bias ? bias[0] : 0.f), act);
+}
+
+template <int BM, int BN, int BK, int WM, int WN, bool VA, bool VB>
+static hipError_t launch_gemm_t(int M, int N, int K, const float* x, int64_t ld_x, const float* W,
+                                const float* bias, int act, float* y, int64_t ld_y, hipStream_t s) {
+    const int tm = (M + BM - 1) / BM;
+    const int tn = (N + BN - 1) / BN;
+    hipLaunchKernelGGL((gemm_bias_act_kernel<BM, BN, BK, WM, WN, VA, VB>), dim3((unsigned)(tm * tn)),
+                       dim3(WM * WN * 64), 0, s, M, N, K, x, ld_x, W, bias, act, y, ld_y, tm, tn);
+    return hipGetLastError();
+}
+
+template <int BM, int BN, int BK, int WM, int WN>
+static hipError_t launch_gemm_v(bool va, bool vb, int M, int N, int K, const float* x, int64_t ld_x, const float* W,
+                                const float* bias, int act, float* y, int64_t ld_y, hipStream_t s) {
+    if (va && vb) return launch_gemm_t<BM, BN, BK, WM, WN, true, true>(M, N, K, x, ld_x, W, bias, act, y, ld_y, s);
+    if (va) return launch_gemm_t<BM, BN, BK, WM, WN, true, false>(M, N, K, x, ld_x, W, bias, act, y, ld_y, s);
+    if (vb) return launch_gemm_t<BM, BN, BK, WM, WN, false, true>(M, N, K, x, ld_x, W, bias, act, y, ld_y, s);
+    return launch_gemm_t<BM, BN, BK, WM, WN, false, false>(M, N, K, x, ld_x, W, bias, act, y, ld_y, s);
+}
+
+static inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+hipError_t launch_linear(int64_t M, int64_t N, int64_t K, const float* x, int64_t ld_x, const float* W,
+                         const float* bias, int act, float* y, int64_t ld_y, hipStream_t s) {
+    const bool va = (ld_x % 4 == 0) && aligned16(x);
+    if (N == 1) {
+        const int64_t blocks = (M + 3) / 4;
+        if (va && aligned16(W))
+            hipLaunchKernelGGL(gemv_bias_act_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, s, (int)M, (int)K,
+                               x, ld_x, W, bias, act, y, ld_y);
+        else
+            hipLaunchKernelGGL(gemv_bias_act_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, s, (int)M, (int)K,
+                               x, ld_x, W, bias, act, y, ld_y);
+        return hipGetLastError();
+    }
+    const bool vb = (K % 4 == 0) && aligned16(W);
+    const int m = (int)M, n = (int)N, k = (int)K;
+    // Tile choice measured on MI355X (inside HIP graphs) for the DLRM layer
+    // shapes: batches too small to give every CU four 64x64 tiles run best on
+    // 32x32 tiles (one 16x16 MFMA block per wave); short K and mid-size
+    // batches on 64x64; large batches on 128x128 once there are >= 4 per CU.
+    const int64_t t64 = ((M + 63) / 64) * ((N + 63) / 64);
+    const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
+    if (t64 < 1024) return launch_gemm_v<32, 32, 32, 2, 2>(va, vb, m, n, k, x, ld_x, W, bias, act, y, ld_y, s);
+    if (K <= 96 || t128 < 1024) return launch_gemm_v<64, 64, 32, 2, 2>(va, vb, m, n, k, x, ld_x, W, bias, act, y, ld_y, s);
+    return launch_gemm_v<128, 128, 32, 2, 2>(va, vb, m, n, k, x, ld_x, W, bias, act, y, ld_y, s);
+}
+
+}  // namespace dlrm

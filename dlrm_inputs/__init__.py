@@ -218,6 +218,17 @@ def make_inputs(w: Workload, device="cpu", int_tables: bool = False, int_dense: 
     return Inputs(w, dense, tables, indices, offsets, bot_w, bot_b, top_w, top_b)
 
 
+def make_indices(w: Workload, device="cpu", seed: int = BASE_SEED) -> List[torch.Tensor]:
+    """Another independently drawn index set (T x (B*L,)) for workload ``w``."""
+    device = torch.device(device)
+    cdf = zipf_cdf(w.rows, w.zipf_s, device) if w.dist == "zipf" else None
+    out = []
+    for t in range(w.num_tables):
+        g = _gen(device, seed + 1000 * w.cfg_id + 500 + t)
+        out.append(draw_indices(w.batch * w.bag, w.rows, w.dist, g, device, w.zipf_s, cdf))
+    return out
+
+
 def ragged_bags(batch: int, max_len: int, gen_seed: int, empty_frac: float = 0.25):
     """Offsets (B,) int64 of bags with random lengths in [0, max_len], some empty.
 
@@ -233,29 +244,42 @@ def ragged_bags(batch: int, max_len: int, gen_seed: int, empty_frac: float = 0.2
     return offs, int(lens.sum())
 
 
-def subset(inp: Inputs, rows: torch.Tensor) -> Inputs:
-    """Inputs restricted to the samples ``rows`` (a 1-D index tensor).
+def subset(inp: Inputs, rows: torch.Tensor, compact_tables: bool = False) -> Inputs:
+    """Inputs restricted to the samples ``rows`` (a 1-D index tensor), on the CPU.
 
     Each selected bag keeps its own indices; offsets are rebuilt for the
-    packed index lists. Pure data selection, used to check sampled outputs of a
-    large batch one sample at a time.
+    packed index lists.  With ``compact_tables`` every table is replaced by
+    just the rows the selected bags reference (indices renumbered to match),
+    so a large resident table need not be copied whole.  Pure data
+    selection, used to check sampled outputs of a large batch.
     """
     rows = rows.to("cpu")
     B = inp.workload.batch
-    new_idx, new_off = [], []
-    for idx, off in zip(inp.indices, inp.offsets):
+    new_idx, new_off, new_tab = [], [], []
+    for tab, idx, off in zip(inp.tables, inp.indices, inp.offsets):
         off_c = off.to("cpu")
-        n = idx.numel()
-        ends = torch.cat([off_c[1:], torch.tensor([n], dtype=torch.int64)]) if B > 1 else torch.tensor([n])
+        idx_c = idx.to("cpu")
+        n = idx_c.numel()
+        ends = torch.cat([off_c[1:], torch.tensor([n], dtype=torch.int64)])
         s, e = off_c[rows], ends[rows]
         lens = e - s
-        take = torch.cat([torch.arange(a, b, dtype=torch.int64) for a, b in zip(s.tolist(), e.tolist())]) \
-            if rows.numel() else torch.zeros(0, dtype=torch.int64)
-        new_idx.append(idx.to("cpu")[take])
+        parts = [torch.arange(a, b, dtype=torch.int64) for a, b in zip(s.tolist(), e.tolist())]
+        take = torch.cat(parts) if parts else torch.zeros(0, dtype=torch.int64)
+        sel = idx_c[take]
+        if compact_tables:
+            uniq, inv = torch.unique(sel, return_inverse=True)
+            if uniq.numel() == 0:
+                uniq = torch.zeros(1, dtype=torch.int64)
+            new_tab.append(tab[uniq.to(tab.device)].to("cpu"))
+            new_idx.append(inv.to(torch.int64))
+        else:
+            new_tab.append(tab.to("cpu"))
+            new_idx.append(sel)
         o = torch.zeros(rows.numel(), dtype=torch.int64)
         if rows.numel() > 1:
             o[1:] = torch.cumsum(lens[:-1], 0)
         new_off.append(o)
     w = inp.workload.with_batch(int(rows.numel()))
-    return Inputs(w, inp.dense.to("cpu")[rows], [t for t in inp.tables], new_idx, new_off,
-                  inp.bot_w, inp.bot_b, inp.top_w, inp.top_b)
+    cpu = lambda xs: [x.to("cpu") for x in xs]
+    return Inputs(w, inp.dense.to("cpu")[rows], new_tab, new_idx, new_off,
+                  cpu(inp.bot_w), cpu(inp.bot_b), cpu(inp.top_w), cpu(inp.top_b))

@@ -1,0 +1,440 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle on MI355X.
+
+Bars:
+* integer / index work bit-exact: the pair-index decoding, bag-size-1 gathers
+  (a copy), and bag sums / dots over integer-valued data, whose every partial
+  sum is exact in fp32 whatever the order;
+* floating point within derived bounds: bag sums within gamma_L * sum|w|,
+  dots within gamma_D * sum|u_d v_d|, Linear layers within
+  gamma_{K+2} * (|x| |W|^T + |b|) + u |y| (layer-wise: the oracle layer is fed
+  the GPU's own fp32 input), with gamma_n = n u / (1 - n u), u = 2^-24;
+* the end-to-end sigmoid output within 1e-5 absolute.
+Workloads are the seeded synthetic ones of dlrm_inputs at their full sizes;
+where the batch is large the oracle checks a seeded sample of outputs, which
+is sound because every output row depends only on its own sample.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import dlrm_embedding_interaction_amd as dl
+import dlrm_inputs as di
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+U = 2.0 ** -24
+E2E_TOL = 1e-5
+
+
+def gamma(n):
+    return n * U / (1 - n * U)
+
+
+def dev():
+    return torch.device("cuda", 0)
+
+
+def log(msg):
+    print(msg, flush=True)
+
+
+def on_gpu(inp):
+    return inp.to(dev())
+
+
+def sample_rows(B, n, seed):
+    if B <= n:
+        return torch.arange(B)
+    g = torch.Generator().manual_seed(seed)
+    return torch.sort(torch.randperm(B, generator=g)[:n]).values
+
+
+# --- pair index decoding --------------------------------------------------------
+
+
+@pytest.mark.parametrize("F", list(range(2, 65)) + [100, 527, 1000, 2049, 4096])
+def test_pair_index_map_is_the_nested_loop_order(F):
+    i, j = dl.pair_index_map(F)
+    ii = i.cpu().numpy()
+    jj = j.cpu().numpy()
+    want_i = np.repeat(np.arange(F), np.arange(F))
+    want_j = np.concatenate([np.arange(r) for r in range(F)])
+    assert np.array_equal(ii, want_i) and np.array_equal(jj, want_j)
+
+
+# --- embedding bags -------------------------------------------------------------
+
+
+@pytest.mark.parametrize("name", ["tiny", "page4", "manytable"])
+def test_embbag_bag1_bitexact(name, orc):
+    w = di.get(name)
+    log(f"embbag bag1 {name}")
+    inp = di.make_inputs(w)
+    g = on_gpu(inp)
+    E = dl.embbag_sum(g.tables, g.indices, g.offsets)
+    torch.cuda.synchronize()
+    ref = orc.embbag_sum(inp.tables, inp.indices, inp.offsets)
+    assert np.array_equal(E.cpu().double().numpy(), ref)
+    # bag size 1 is index_select
+    for t in range(w.num_tables):
+        assert torch.equal(E[:, t, :], torch.index_select(g.tables[t], 0, g.indices[t]))
+
+
+@pytest.mark.parametrize("D", [1, 3, 4, 6, 16, 17, 48, 64, 100, 128, 256, 512, 1024])
+@pytest.mark.parametrize("L", [1, 20])
+def test_embbag_integer_tables_bitexact_all_dims(D, L, orc):
+    w = di.custom(f"int_d{D}", 67, 3, 5, 300, D, L, (3, D), cfg_id=11)
+    log(f"embbag int D={D} L={L}")
+    inp = di.make_inputs(w, int_tables=True)
+    g = on_gpu(inp)
+    E = dl.embbag_sum(g.tables, g.indices, g.offsets)
+    torch.cuda.synchronize()
+    assert np.array_equal(E.cpu().double().numpy(), orc.embbag_sum(inp.tables, inp.indices, inp.offsets))
+
+
+def test_embbag_ragged_and_empty_bags_bitexact(orc):
+    T, B, D = 6, 301, 64
+    tables, idx, off = [], [], []
+    gen = torch.Generator().manual_seed(7)
+    for t in range(T):
+        o, n = di.ragged_bags(B, 30, 900 + t, empty_frac=0.3)
+        tables.append(torch.randint(-8, 9, (97, D), generator=gen).float())
+        idx.append(torch.randint(0, 97, (n,), generator=gen))
+        off.append(o)
+    # a table whose every bag is empty, and one whose bags are all in the last sample
+    off[4] = torch.zeros(B, dtype=torch.int64)
+    idx[4] = torch.randint(0, 97, (33,), generator=gen)
+    off[5] = torch.zeros(B, dtype=torch.int64)
+    idx[5] = torch.zeros(0, dtype=torch.int64)
+    E = dl.embbag_sum([t.cuda() for t in tables], [i.cuda() for i in idx], [o.cuda() for o in off])
+    torch.cuda.synchronize()
+    ref = orc.embbag_sum(tables, idx, off)
+    assert np.array_equal(E.cpu().double().numpy(), ref)
+    ref_t = torch.nn.functional.embedding_bag(idx[0], tables[0], off[0], mode="sum")
+    assert torch.equal(E[:, 0].cpu(), ref_t)
+
+
+def test_embbag_float_multi_hot_within_bound(orc):
+    w = di.custom("float_l20", 513, 3, 4, 5000, 128, 20, (3, 128), dist="zipf", cfg_id=12)
+    inp = di.make_inputs(w)
+    g = on_gpu(inp)
+    E = dl.embbag_sum(g.tables, g.indices, g.offsets).cpu().double().numpy()
+    ref = orc.embbag_sum(inp.tables, inp.indices, inp.offsets)
+    mag = orc.embbag_sum([t.abs() for t in inp.tables], inp.indices, inp.offsets)
+    err = np.abs(E - ref)
+    assert np.all(err <= gamma(w.bag) * mag + 1e-30), err.max()
+
+
+def test_embbag_unaligned_tables_take_the_scalar_path(orc):
+    gen = torch.Generator().manual_seed(3)
+    base = [torch.randint(-8, 9, (200 * 64 + 1,), generator=gen).float() for _ in range(2)]
+    tables_cpu = [b[1:].view(200, 64) for b in base]           # 4-byte offset: not 16-byte aligned
+    idx = [torch.randint(0, 200, (90,), generator=gen) for _ in range(2)]
+    off = [torch.arange(45) * 2 for _ in range(2)]
+    tables_gpu = [b.cuda()[1:].view(200, 64) for b in base]
+    assert tables_gpu[0].data_ptr() % 16 != 0
+    E = dl.embbag_sum(tables_gpu, [i.cuda() for i in idx], [o.cuda() for o in off])
+    torch.cuda.synchronize()
+    assert np.array_equal(E.cpu().double().numpy(), orc.embbag_sum(tables_cpu, idx, off))
+
+
+def test_check_indices_counts_bad_data():
+    gen = torch.Generator().manual_seed(5)
+    idx = [torch.randint(0, 50, (40,), generator=gen).cuda(), torch.randint(0, 60, (40,), generator=gen).cuda()]
+    off = [torch.arange(20).cuda() * 2, torch.arange(20).cuda() * 2]
+    assert dl.check_indices([50, 60], idx, off) == 0
+    idx[0][3] = 50
+    idx[1][7] = -2
+    off[1][5] = 100          # passes n_indices, and bag 5 > bag 6 start
+    assert dl.check_indices([50, 60], idx, off) == 4
+
+
+# --- interaction ------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("T,D", [(1, 64), (3, 16), (3, 64), (8, 5), (26, 128), (32, 64), (63, 16), (64, 33)])
+@pytest.mark.parametrize("concat", [True, False])
+def test_interact_integer_bitexact(T, D, concat, orc):
+    B = 129
+    gen = torch.Generator().manual_seed(T * 1000 + D)
+    x = torch.randint(-16, 17, (B, D), generator=gen).float()
+    E = torch.randint(-16, 17, (B, T, D), generator=gen).float()
+    out = dl.interact_lower_tri(x.cuda(), E.cuda(), concat_dense=concat)
+    torch.cuda.synchronize()
+    Z = orc.interact(x.double().numpy(), E.double().numpy())
+    want = np.concatenate([x.double().numpy(), Z], 1) if concat else Z
+    assert np.array_equal(out.cpu().double().numpy(), want)
+
+
+@pytest.mark.parametrize("T,D", [(3, 64), (32, 64), (26, 128)])
+def test_interact_float_within_bound(T, D, orc):
+    B = 1000
+    gen = torch.Generator().manual_seed(17)
+    x = torch.randn((B, D), generator=gen)
+    E = torch.randn((B, T, D), generator=gen)
+    out = dl.interact_lower_tri(x.cuda(), E.cuda(), concat_dense=False).cpu().double().numpy()
+    Z = orc.interact(x.double().numpy(), E.double().numpy())
+    mag = orc.interact(x.abs().double().numpy(), E.abs().double().numpy())
+    assert np.all(np.abs(out - Z) <= gamma(D) * mag + 1e-30)
+
+
+def test_interact_leaves_other_columns_untouched(orc):
+    B, T, D = 37, 4, 16
+    P = (T + 1) * T // 2
+    gen = torch.Generator().manual_seed(9)
+    xw = torch.randint(-4, 5, (B, D + 9), generator=gen).float().cuda()
+    x = xw[:, 3:3 + D]                              # strided view, ld 25, offset 3
+    E = torch.randint(-4, 5, (B, T, D), generator=gen).float().cuda()
+    out = torch.full((B, D + P + 7), -777.0, device="cuda")
+    dl.interact_lower_tri(x, E, concat_dense=True, out=out)
+    torch.cuda.synchronize()
+    o = out.cpu()
+    assert torch.all(o[:, D + P:] == -777.0)
+    Z = orc.interact(x.cpu().double().numpy(), E.cpu().double().numpy())
+    assert np.array_equal(o[:, :D].double().numpy(), x.cpu().double().numpy())
+    assert np.array_equal(o[:, D:D + P].double().numpy(), Z)
+
+
+# --- linear layers --------------------------------------------------------------
+
+
+def _linear_check(orc, x, W, b, act, y):
+    x64 = x.cpu().double().numpy()
+    Wc = W.cpu().numpy()
+    bc = b.cpu().numpy() if b is not None else None
+    ref = orc.linear(x64, Wc, bc, 0)
+    mag = np.abs(x64) @ np.abs(Wc.astype(np.float64)).T + (np.abs(bc.astype(np.float64)) if bc is not None else 0)
+    K = W.shape[1]
+    bound = gamma(K + 2) * mag + U * np.abs(ref) + 1e-30
+    got = y.cpu().double().numpy()
+    if act == dl.ACT_RELU:
+        ref = np.maximum(ref, 0.0)
+    if act == dl.ACT_SIGMOID:
+        ref = 1.0 / (1.0 + np.exp(-ref))
+        bound = 0.25 * bound + 4 * U
+    err = np.abs(got - ref)
+    assert np.all(err <= bound), (err.max(), (err / bound).max())
+
+
+SHAPES = [
+    (2048, 512, 13), (2048, 256, 512), (2048, 64, 256), (2048, 512, 70), (2048, 512, 592),
+    (2048, 1, 256), (8, 32, 4), (8, 16, 32), (8, 32, 22), (8, 1, 32),
+    (33, 17, 5), (1, 1, 1), (1, 7, 3), (130, 129, 127), (1000, 300, 200), (4096, 1024, 479), (4096, 128, 256),
+]
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+@pytest.mark.parametrize("act", [0, 1, 2])
+def test_linear_within_bound(M, N, K, act, orc):
+    gen = torch.Generator().manual_seed(M * 7 + N * 13 + K)
+    x = torch.randn((M, K), generator=gen)
+    W = torch.randn((N, K), generator=gen) * K ** -0.5
+    b = torch.randn((N,), generator=gen) * K ** -0.5
+    y = dl.linear_bias_act(x.cuda(), W.cuda(), b.cuda(), act)
+    torch.cuda.synchronize()
+    _linear_check(orc, x, W, b, act, y)
+
+
+def test_linear_no_bias_and_strided_io(orc):
+    gen = torch.Generator().manual_seed(1)
+    xw = torch.randn((300, 80), generator=gen).cuda()
+    x = xw[:, 5:75]                                  # ld 80, K 70, unaligned start
+    W = torch.randn((96, 70), generator=gen).cuda()
+    yw = torch.full((300, 100), 5.0, device="cuda")
+    y = yw[:, :96]
+    dl.linear_bias_act(x, W, None, dl.ACT_NONE, out=y)
+    torch.cuda.synchronize()
+    assert torch.all(yw[:, 96:] == 5.0)
+    _linear_check(orc, x, W, None, 0, y)
+
+
+def test_linear_integer_exact():
+    gen = torch.Generator().manual_seed(2)
+    x = torch.randint(-3, 4, (257, 70), generator=gen).float()
+    W = torch.randint(-3, 4, (130, 70), generator=gen).float()
+    b = torch.randint(-3, 4, (130,), generator=gen).float()
+    y = dl.linear_bias_act(x.cuda(), W.cuda(), b.cuda(), dl.ACT_RELU).cpu()
+    ref = torch.relu(x.double() @ W.double().t() + b.double())
+    assert torch.equal(y.double(), ref)
+
+
+# --- whole forward ------------------------------------------------------------------
+
+
+def _forward_check(inp_cpu, g, orc, rows=None, tol=E2E_TOL):
+    model = dl.Model.from_inputs(g)
+    out = model.forward(g.dense, g.indices, g.offsets)
+    torch.cuda.synchronize()
+    got = out.cpu().double().numpy()
+    if rows is None:
+        ref = oracle.forward_inputs(inp_cpu, oracle=orc)
+        err = np.abs(got - ref)
+    else:
+        sub = di.subset(g, rows, compact_tables=True)
+        ref = oracle.forward_inputs(sub, oracle=orc)
+        err = np.abs(got[rows.numpy()] - ref)
+    assert err.max() <= tol, err.max()
+    return model, out, err.max()
+
+
+@pytest.mark.parametrize("name", ["tiny", "page4", "manytable"])
+def test_forward_e2e(name, orc):
+    log(f"forward {name}")
+    inp = di.make_inputs(di.get(name))
+    _, _, e = _forward_check(inp, on_gpu(inp), orc)
+    log(f"  max |err| = {e:.3g}")
+
+
+def test_forward_layerwise_through_standalone_calls(orc):
+    """Compose the four calls by hand and check each stage on the GPU's own inputs."""
+    inp = di.make_inputs(di.PAGE4)
+    g = on_gpu(inp)
+    h = g.dense
+    for W, b in zip(g.bot_w, g.bot_b):
+        y = dl.linear_bias_act(h, W, b, dl.ACT_RELU)
+        _linear_check(orc, h, W, b, dl.ACT_RELU, y)
+        h = y
+    x = h
+    E = dl.embbag_sum(g.tables, g.indices, g.offsets)
+    assert np.array_equal(E.cpu().double().numpy(), orc.embbag_sum(inp.tables, inp.indices, inp.offsets))
+    R = dl.interact_lower_tri(x, E, concat_dense=True)
+    Zr = orc.interact(x.cpu().double().numpy(), E.cpu().double().numpy())
+    mag = orc.interact(x.abs().cpu().double().numpy(), E.abs().cpu().double().numpy())
+    D = x.shape[1]
+    assert np.all(np.abs(R[:, D:].cpu().double().numpy() - Zr) <= gamma(D) * mag + 1e-30)
+    h = R
+    n = len(g.top_w)
+    for l, (W, b) in enumerate(zip(g.top_w, g.top_b)):
+        act = dl.ACT_SIGMOID if l == n - 1 else dl.ACT_RELU
+        y = dl.linear_bias_act(h, W, b, act)
+        _linear_check(orc, h, W, b, act, y)
+        h = y
+    # and the fused forward agrees with the composition
+    out = dl.Model.from_inputs(g).forward(g.dense, g.indices, g.offsets)
+    assert torch.allclose(out, h[:, 0], atol=1e-6, rtol=0)
+
+
+@pytest.mark.parametrize("B,T", [(16, 1), (16, 32), (64, 8), (256, 4), (2048, 16), (4096, 1), (16384, 8),
+                                 (16384, 32)])
+def test_forward_sweep_cells(B, T, orc):
+    log(f"sweep cell b={B} t={T}")
+    w = di.sweep(B, T)
+    g = di.make_inputs(w, device=dev())
+    rows = sample_rows(B, 512, B + T)
+    _forward_check(None, g, orc, rows=rows)
+
+
+def test_forward_stress_sampled(orc):
+    """The 26-table, 1M-row, d=128, bag-20 Zipf workload at full size (13.3 GB of tables)."""
+    log("stress: generating 13.3 GB of tables on the GPU")
+    g = di.make_inputs(di.STRESS, device=dev())
+    rows = sample_rows(di.STRESS.batch, 384, 5)
+    _, _, e = _forward_check(None, g, orc, rows=rows)
+    log(f"  stress max |err| on {rows.numel()} sampled outputs = {e:.3g}")
+    del g
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("B", [1, 2, 3, 5, 17, 100])
+def test_forward_small_and_ragged_batches(B, orc):
+    w = di.custom(f"small_b{B}", B, 13, 7, 1000, 64, 1, (13, 64, 64), hidden_top=(64, 32), cfg_id=13)
+    inp = di.make_inputs(w)
+    _forward_check(inp, on_gpu(inp), orc)
+
+
+def test_forward_multi_hot_ragged_bags(orc):
+    w = di.custom("ragged_fwd", 211, 5, 9, 500, 32, 1, (5, 48, 32), hidden_top=(40,), cfg_id=14)
+    inp = di.make_inputs(w)
+    gen = torch.Generator().manual_seed(21)
+    for t in range(w.num_tables):
+        off, n = di.ragged_bags(w.batch, 12, 1200 + t, empty_frac=0.25)
+        inp.offsets[t] = off
+        inp.indices[t] = torch.randint(0, w.rows, (n,), generator=gen)
+    _forward_check(inp, on_gpu(inp), orc)
+
+
+def test_forward_zero_last_layer_gives_exactly_half():
+    inp = di.make_inputs(di.PAGE4)
+    inp.top_w[-1].zero_()
+    inp.top_b[-1].zero_()
+    g = on_gpu(inp)
+    out = dl.Model.from_inputs(g).forward(g.dense, g.indices, g.offsets)
+    assert torch.all(out == 0.5)
+
+
+def test_forward_rejects_bad_shapes():
+    inp = on_gpu(di.make_inputs(di.TINY))
+    with pytest.raises(dl.DlrmError) as e:
+        dl.Model(inp.tables, inp.bot_w, inp.bot_b, inp.top_w[1:], inp.top_b[1:]).forward(
+            inp.dense, inp.indices, inp.offsets)
+    assert e.value.code == dl.DLRM_E_SHAPE
+
+
+def test_forward_graph_capture_replays_match_eager():
+    inp = on_gpu(di.make_inputs(di.PAGE4))
+    model = dl.Model.from_inputs(inp)
+    B = inp.workload.batch
+    out = torch.empty(B, device="cuda")
+    ws = model.workspace(B)
+    args = model.forward_args(inp.dense, inp.indices, inp.offsets)
+    model.forward(inp.dense, inp.indices, inp.offsets, out=out, workspace=ws, args=args)   # warm up
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            model.forward(inp.dense, inp.indices, inp.offsets, out=out, workspace=ws, args=args)
+    torch.cuda.current_stream().wait_stream(s)
+    gen = torch.Generator(device="cuda").manual_seed(3)
+    for rep in range(4):
+        inp.dense.copy_(torch.rand(inp.dense.shape, generator=gen, device="cuda"))
+        for t in range(len(inp.indices)):
+            inp.indices[t].copy_(torch.randint(0, inp.workload.rows, (B,), generator=gen, device="cuda"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        eager = model.forward(inp.dense, inp.indices, inp.offsets)
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {rep} differs"
+
+
+# --- fused bag gather + interaction ---------------------------------------------
+
+
+@pytest.mark.parametrize("T,D,L", [(3, 16, 1), (3, 64, 1), (32, 64, 1), (26, 128, 20), (5, 6, 3), (8, 512, 2)])
+def test_embbag_interact_integer_bitexact(T, D, L, orc):
+    w = di.custom(f"fused_{T}_{D}_{L}", 150, 3, T, 400, D, L, (3, D), cfg_id=15)
+    inp = di.make_inputs(w, int_tables=True)
+    gen = torch.Generator().manual_seed(T + D)
+    x = torch.randint(-2, 3, (w.batch, D), generator=gen).float()
+    g = on_gpu(inp)
+    out = dl.embbag_interact(g.tables, g.indices, g.offsets, x.cuda(), concat_dense=True)
+    torch.cuda.synchronize()
+    E = orc.embbag_sum(inp.tables, inp.indices, inp.offsets)
+    Z = orc.interact(x.double().numpy(), E)
+    assert np.array_equal(out.cpu().double().numpy(), np.concatenate([x.double().numpy(), Z], 1))
+
+
+def test_embbag_interact_in_place_beside_x(orc):
+    """x = R[:, :D] and Z written to R[:, D:D+P], the layout the forward uses."""
+    inp = di.make_inputs(di.MANYTABLE)
+    g = on_gpu(inp)
+    B, D, T = 2048, 64, 32
+    P = (T + 1) * T // 2
+    ld = 596
+    gen = torch.Generator().manual_seed(4)
+    R = torch.full((B, ld), 123.0, device="cuda")
+    x = torch.randn((B, D), generator=gen)
+    R[:, :D] = x.cuda()
+    dl.embbag_interact(g.tables, g.indices, g.offsets, R, concat_dense=False, out=R[:, D:])
+    torch.cuda.synchronize()
+    Rc = R.cpu()
+    assert torch.equal(Rc[:, :D], x) and torch.all(Rc[:, D + P:] == 123.0)
+    E = orc.embbag_sum(inp.tables, inp.indices, inp.offsets)
+    Z = orc.interact(x.double().numpy(), E)
+    mag = orc.interact(x.abs().double().numpy(), np.abs(E))
+    assert np.all(np.abs(Rc[:, D:D + P].double().numpy() - Z) <= gamma(D) * mag + 1e-30)

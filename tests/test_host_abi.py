@@ -1,0 +1,164 @@
+"""Host-side checks of the C-ABI library that need no GPU.
+
+The library must load and export every function include/dlrm_mi355x.h
+declares.  Argument validation runs on the host before any HIP call, so the
+error paths (NULL pointers, inconsistent shapes, unsupported sizes, missing
+workspace) can be exercised here without a device; no compute call is made.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import dlrm_embedding_interaction_amd as dl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dlrm_mi355x.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^[a-z_][\w\s\*]*?\b(dlrm_\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return dl.load()
+
+
+def test_header_declares_the_hot_path_calls():
+    names = declared_functions()
+    for n in ("dlrm_embbag_sum", "dlrm_interact_lower_tri", "dlrm_linear_bias_act", "dlrm_forward"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(lib, n), f"{n} not exported"
+
+
+def test_status_strings_and_abi_version(lib):
+    assert lib.dlrm_abi_version() == dl.ABI_VERSION
+    for code in range(7):
+        s = lib.dlrm_status_string(code).decode()
+        assert s.startswith("DLRM_")
+    assert b"unknown" in lib.dlrm_status_string(99)
+
+
+def _model(ln_bot, ln_top, T, D, rows=100):
+    keep = dl._i64s(ln_bot), dl._i64s(ln_top), dl._i64s([rows] * T)
+    fake = dl._vp * 64
+    ptrs = fake(*([4096] * 64))  # never dereferenced: validation fails or only sizes are read
+    m = dl._Model(len(ln_bot), ctypes.cast(keep[0], dl._i64p), len(ln_top), ctypes.cast(keep[1], dl._i64p), T, D,
+                  ctypes.cast(keep[2], dl._i64p), ptrs, ptrs, ptrs, ptrs, ptrs)
+    return m, (keep, ptrs)
+
+
+def _round_up(v, a):
+    return (v + a - 1) // a * a
+
+
+@pytest.mark.parametrize("B,ln_bot,ln_top,T,D", [
+    (8, [4, 32, 16], [22, 32, 1], 3, 16),
+    (2048, [13, 512, 256, 64], [70, 512, 256, 1], 3, 64),
+    (2048, [13, 512, 256, 64], [592, 512, 256, 1], 32, 64),
+    (65536, [13, 512, 256, 128], [479, 1024, 1024, 512, 256, 1], 26, 128),
+    (5, [3, 4], [10, 1], 3, 4),
+])
+def test_workspace_bytes_formula(lib, B, ln_bot, ln_top, T, D):
+    m, keep = _model(ln_bot, ln_top, T, D)
+    P = (T + 1) * T // 2
+    ldR = _round_up(D + P, 4)
+    hidden = ln_bot[1:-1] + ln_top[1:-1]
+    ldH = _round_up(max(hidden) if hidden else 0, 4)
+    want = _round_up(B * ldR * 4, 256) + 2 * _round_up(B * ldH * 4, 256)
+    assert lib.dlrm_forward_workspace_bytes(ctypes.byref(m), B) == want
+
+
+@pytest.mark.parametrize("ln_bot,ln_top,T,D,B", [
+    ([13, 8, 4], [9, 8, 1], 3, 4, 16),      # ln_top[0] != D + P
+    ([13, 8, 4], [10, 8, 2], 3, 4, 16),     # last top width != 1
+    ([13, 8, 5], [10, 8, 1], 3, 4, 16),     # last bottom width != D
+    ([4], [10, 8, 1], 3, 4, 16),            # no bottom layer
+    ([13, 8, 4], [10, 8, 1], 3, 4, 0),      # empty batch
+])
+def test_invalid_models_are_rejected(lib, ln_bot, ln_top, T, D, B):
+    m, keep = _model(ln_bot, ln_top, T, D)
+    assert lib.dlrm_forward_workspace_bytes(ctypes.byref(m), B) == 0
+    one = dl._ptrs([])
+    rc = lib.dlrm_forward(ctypes.byref(m), B, 4096, one, dl._i64s([1] * T), one, 4096, 4096, 1 << 30, None)
+    assert rc == dl.DLRM_E_SHAPE
+
+
+def test_mini_dlrm_shape_from_the_pages_is_valid(lib):
+    # dlrm_megakernel.rs unit test shape_invariants: ln_bot [13,8,4], m_spa 4, 3 tables, ln_top [10,8,1]
+    m, keep = _model([13, 8, 4], [10, 8, 1], 3, 4)
+    assert lib.dlrm_forward_workspace_bytes(ctypes.byref(m), 2048) > 0
+
+
+def test_forward_rejects_missing_or_small_workspace(lib):
+    m, keep = _model([13, 8, 4], [10, 8, 1], 3, 4)
+    need = lib.dlrm_forward_workspace_bytes(ctypes.byref(m), 16)
+    fake = (dl._vp * 3)(4096, 4096, 4096)
+    n = dl._i64s([16, 16, 16])
+    assert lib.dlrm_forward(ctypes.byref(m), 16, 4096, fake, n, fake, 4096, None, need, None) == dl.DLRM_E_WORKSPACE
+    assert lib.dlrm_forward(ctypes.byref(m), 16, 4096, fake, n, fake, 4096, 4096, need - 1, None) == dl.DLRM_E_WORKSPACE
+    assert lib.dlrm_forward(ctypes.byref(m), 16, 4096, fake, n, fake, 4096, 4096 + 16, need, None) == dl.DLRM_E_WORKSPACE
+    assert lib.dlrm_forward(None, 16, 4096, fake, n, fake, 4096, 4096, need, None) == dl.DLRM_E_NULL
+    assert lib.dlrm_forward(ctypes.byref(m), 16, None, fake, n, fake, 4096, 4096, need, None) == dl.DLRM_E_NULL
+
+
+def test_linear_argument_errors(lib):
+    f = lib.dlrm_linear_bias_act
+    assert f(4, 4, 4, None, 4, 4096, None, 0, 4096, 4, None) == dl.DLRM_E_NULL
+    assert f(0, 4, 4, 4096, 4, 4096, None, 0, 4096, 4, None) == dl.DLRM_E_SHAPE
+    assert f(4, 4, 8, 4096, 4, 4096, None, 0, 4096, 4, None) == dl.DLRM_E_SHAPE   # ld_x < K
+    assert f(4, 8, 4, 4096, 4, 4096, None, 0, 4096, 4, None) == dl.DLRM_E_SHAPE   # ld_y < N
+    assert f(4, 4, 4, 4096, 4, 4096, None, 7, 4096, 4, None) == dl.DLRM_E_SHAPE   # unknown activation
+
+
+def test_embbag_argument_errors(lib):
+    f = lib.dlrm_embbag_sum
+    p = (dl._vp * 65)(*([4096] * 65))
+    n = dl._i64s([1] * 65)
+    assert f(65, 4, 4, p, n, p, n, p, 4096, None) == dl.DLRM_E_UNSUPPORTED
+    assert f(0, 4, 4, p, n, p, n, p, 4096, None) == dl.DLRM_E_SHAPE
+    assert f(2, 4, 2048, p, n, p, n, p, 4096, None) == dl.DLRM_E_UNSUPPORTED  # dim above 1024
+    assert f(2, 4, 4, p, n, p, n, p, None, None) == dl.DLRM_E_NULL
+    z = (dl._vp * 2)(4096, None)
+    assert f(2, 4, 4, z, n, p, n, p, 4096, None) == dl.DLRM_E_NULL
+    neg = dl._i64s([1, -1])
+    assert f(2, 4, 4, p, n, p, neg, p, 4096, None) == dl.DLRM_E_SHAPE
+
+
+def test_interact_argument_errors(lib):
+    f = lib.dlrm_interact_lower_tri
+    assert f(4, 3, 16, None, 16, 4096, 4096, 22, 1, None) == dl.DLRM_E_NULL
+    assert f(4, 3, 16, 4096, 8, 4096, 4096, 22, 1, None) == dl.DLRM_E_SHAPE     # ld_x < dim
+    assert f(4, 3, 16, 4096, 16, 4096, 4096, 21, 1, None) == dl.DLRM_E_SHAPE    # ld_out < D + P
+    assert f(4, 3, 16, 4096, 16, 4096, 4096, 5, 0, None) == dl.DLRM_E_SHAPE     # ld_out < P
+    assert f(4, 64, 1024, 4096, 1024, 4096, 4096, 4096, 0, None) == dl.DLRM_E_UNSUPPORTED  # LDS
+
+
+def test_fused_bag_interaction_argument_errors(lib):
+    f = lib.dlrm_embbag_interact
+    p = (dl._vp * 3)(4096, 4096, 4096)
+    n = dl._i64s([4, 4, 4])
+    assert f(3, 4, 16, p, n, p, n, p, None, 16, 4096, 22, 1, None) == dl.DLRM_E_NULL
+    assert f(3, 4, 16, p, n, p, n, p, 4096, 8, 4096, 22, 1, None) == dl.DLRM_E_SHAPE
+    assert f(3, 4, 16, p, n, p, n, p, 4096, 16, 4096, 21, 1, None) == dl.DLRM_E_SHAPE
+    assert f(3, 4, 16, p, n, p, n, p, 4096, 16, 4096, 5, 0, None) == dl.DLRM_E_SHAPE
+    assert f(65, 4, 16, p, n, p, n, p, 4096, 16, 4096, 4096, 0, None) == dl.DLRM_E_UNSUPPORTED
+
+
+def test_pair_map_and_check_argument_errors(lib):
+    assert lib.dlrm_pair_index_map(1, 4096, 4096, None) == dl.DLRM_E_SHAPE
+    assert lib.dlrm_pair_index_map(4, None, 4096, None) == dl.DLRM_E_NULL
+    p = (dl._vp * 2)(4096, 4096)
+    n = dl._i64s([1, 1])
+    assert lib.dlrm_embbag_check_indices(2, 4, n, p, n, p, None, None) == dl.DLRM_E_NULL
+    assert lib.dlrm_embbag_check_indices(0, 4, n, p, n, p, 4096, None) == dl.DLRM_E_SHAPE
