@@ -29,6 +29,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, GB/s
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_counters.md")
+CSRC = os.path.join(ROOT, "dlrm_embedding_interaction_amd", "csrc")
 FP32_MFMA_PEAK_TFLOPS = 157.3   # MI355X dense fp32 matrix
 
 
@@ -44,6 +46,10 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--secondary", action="store_true", help="also time the 32-table workload")
     p.add_argument("--kernel-reps", type=int, default=50)
+    p.add_argument("--sweep", metavar="OUT_JSON", default=None,
+                   help="time every batch x tables cell of the sweep grid, write them to OUT_JSON, print no line")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="also run a 512 MiB device copy, the reference kernel for HBM byte counters")
     return p.parse_args()
 
 
@@ -84,6 +90,11 @@ def main():
         sys.exit(1)
     dl.load(build_if_missing=False)
     dev = torch.device("cuda", 0)
+    if args.sweep:
+        run_sweep(torch, dl, di, dev, args)
+        return
+    if args.copy_calibration:
+        copy_calibration(torch, dev)
     w = di.get(args.workload)
 
     res = run_workload(torch, dl, di, w, dev, args)
@@ -100,7 +111,7 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
-        "data": "synthetic (seeded; dense U[0,1), tables N(0,1/D), uniform indices, bag 1)",
+        "data": f"synthetic (seeded; dense U[0,1), tables N(0,1/D), {w.dist} indices, bag {w.bag})",
         "config": {"workload": w.name, "batch": w.batch, "num_tables": w.num_tables, "rows_per_table": w.rows,
                    "dim": w.dim, "bag": w.bag, "ln_bot": list(w.ln_bot), "ln_top": list(w.ln_top),
                    "mode": "eager" if args.eager else "hip_graph", "index_sets": args.index_sets},
@@ -171,8 +182,9 @@ def run_workload(torch, dl, di, w, dev, args):
     ms = (t1 - t0) * 1e3 / args.steps
 
     kernels = time_stages(torch, dl, model, inp, idx_sets, ws, w, args.kernel_reps)
-    roof = roofline(kernels, dominant=True)
-    roof_emb = roofline([k for k in kernels if k["name"] == "emb_interact"], dominant=True)
+    traffic = counted_traffic(w.name)
+    roof = roofline(kernels, dominant=True, traffic=traffic)
+    roof_emb = roofline([k for k in kernels if k["name"] == "emb_interact"], dominant=True, traffic=traffic)
     del inp, model, idx_sets, ws, argsets
     torch.cuda.empty_cache()
     return dict(ms_per_step=ms, samples_per_s=B / (ms * 1e-3), kernels=kernels, roofline=roof, roofline_emb=roof_emb)
@@ -249,19 +261,78 @@ def time_stages(torch, dl, model, inp, idx_sets, ws, w, reps):
     return out
 
 
-def roofline(kernels, dominant=True):
+def kernel_source_hash() -> str:
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(CSRC, "*"))):
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def counted_traffic(workload: str) -> dict:
+    """HBM bytes per dispatch of each stage from the committed counter summary,
+    or {} when the kernel sources have changed since the counters were taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return {}
+    text = open(TRAFFIC_FILE).read()
+    want = f"kernel-source-sha256: {kernel_source_hash()}"
+    if want not in text:
+        return {}
+    out = {}
+    for line in text.splitlines():
+        cells = [c.strip() for c in line.strip().strip("|").split("|")]
+        if len(cells) == 7 and cells[0] == workload:
+            out[cells[1]] = int(cells[6])
+    return out
+
+
+def roofline(kernels, dominant=True, traffic=None):
     k = max(kernels, key=lambda s: s["us"])
     sec = k["us"] * 1e-6
+    tr = (traffic or {}).get(k["name"])
     if k["kind"] == "mfma":
         achieved = k["flops"] / sec / 1e12
         return {"kernel": k["name"], "bound": "mfma", "achieved": achieved, "peak": FP32_MFMA_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": achieved / FP32_MFMA_PEAK_TFLOPS, "traffic": None,
+                "unit": "TFLOP/s", "frac": achieved / FP32_MFMA_PEAK_TFLOPS, "traffic": tr,
                 "us_per_launch": k["us"], "flops_per_launch": k["flops"],
                 "shape": [k.get("M"), k.get("N"), k.get("K")]}
     achieved = k["bytes"] / sec / 1e9
     return {"kernel": k["name"], "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBPS, "traffic": None, "us_per_launch": k["us"],
+            "frac": achieved / HBM_PEAK_GBPS, "traffic": tr, "us_per_launch": k["us"],
             "bytes_per_launch": k["bytes"]}
+
+
+def copy_calibration(torch, dev, nbytes=512 << 20, reps=5):
+    """A plain device-to-device copy of known size: its FETCH_SIZE / WRITE_SIZE per
+    dispatch scale the counters of the measured kernels to bytes."""
+    a = torch.ones(nbytes // 4, device=dev)
+    b = torch.empty_like(a)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(f"[bench] copy calibration: {reps} copies of {nbytes} bytes", file=sys.stderr, flush=True)
+    del a, b
+
+
+def run_sweep(torch, dl, di, dev, args):
+    rows = []
+    for T in di.SWEEP_TABLES:
+        for B in di.SWEEP_BATCHES:
+            w = di.sweep(B, T)
+            a = argparse.Namespace(**vars(args))
+            a.steps, a.warmup = max(20, min(args.steps, 200)), 10
+            r = run_workload(torch, dl, di, w, dev, a)
+            emb = next(k for k in r["kernels"] if k["name"] == "emb_interact")
+            row = dict(batch=B, tables=T, us_per_forward=r["ms_per_step"] * 1e3, samples_per_s=r["samples_per_s"],
+                       emb_interact_us=emb["us"], emb_interact_GBps=r["roofline_emb"]["achieved"],
+                       kernels={k["name"]: k["us"] for k in r["kernels"]})
+            rows.append(row)
+            print(f"[sweep] b={B:6d} t={T:2d}  {row['us_per_forward']:9.2f} us/fwd  "
+                  f"emb {emb['us']:8.2f} us {row['emb_interact_GBps']:8.1f} GB/s", file=sys.stderr, flush=True)
+    with open(args.sweep, "w") as f:
+        json.dump(rows, f, indent=1)
 
 
 def cpu_baseline(w, seconds):

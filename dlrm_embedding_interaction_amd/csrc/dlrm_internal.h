@@ -13,6 +13,7 @@ namespace dlrm {
 constexpr int kMaxDim = 1024;                       // longest embedding row supported
 constexpr size_t kInteractLdsBudget = 32 * 1024;     // target LDS per interaction block
 constexpr size_t kMaxLdsBytes = 64 * 1024;           // hard LDS limit per block
+constexpr int kRowPad = 4;                           // floats of padding per LDS feature row
 
 // Arguments of the device-side bag-data check.
 struct CheckArgs {

@@ -19,11 +19,16 @@
 //    (global_load_dwordx4), so a wave64 reads 1 KiB per instruction; each
 //    group keeps U bags in flight and prefetches R row indices per bag, so a
 //    wave has U*R independent row loads outstanding;
-//  * the fused kernel places the F vectors of each of its samples in LDS,
-//    then every G-lane group takes one flat pair index p at a time, decodes
-//    (i, j) in closed form, dots the two LDS rows and reduces across the group
-//    with DPP / ds_swizzle; the P results of a sample are staged in LDS and
-//    written as one contiguous row segment.
+//  * the fused kernel places the F vectors of each of its samples in LDS
+//    (rows padded by 4 floats so that rows 16 apart are the first to share
+//    banks).  With few vectors (F <= 12) every G-lane group takes one flat
+//    pair index p at a time, decodes (i, j) in closed form, dots the two LDS
+//    rows and reduces across the group with DPP / ds_swizzle.  With more
+//    vectors each lane owns a 4x4 block of the strict lower triangle (block
+//    index decoded with the same closed form) and accumulates its 16 dots
+//    over d from float4 LDS reads, 8 reads per 64 FMAs and no cross-lane
+//    traffic.  The P results of a sample are staged in LDS and written as
+//    one contiguous row segment.
 #include "dlrm_device.h"
 #include "dlrm_internal.h"
 
@@ -140,8 +145,9 @@ __global__ __launch_bounds__(kBlock) void embbag_sum_kernel(TableArgs ta, int T,
 }
 
 // ---- interaction, with the bags either gathered (GATHER) or read from E ------
-// LDS: S[spb][F][D] then Zs[spb][P].
-template <int VEC, int G, int C, int U, int R, bool GATHER>
+// LDS: S[spb][F][D + kRowPad] then Zs[spb][P].  RT = 0: lane-group dots;
+// RT = 4: per-lane 4x4 register blocks of the triangle.
+template <int VEC, int G, int C, int U, int R, bool GATHER, int RT>
 __global__ __launch_bounds__(kBlock) void interact_kernel(TableArgs ta, const float* __restrict__ emb, int T,
                                                           int D, int64_t B, int spb, const float* x,
                                                           int64_t ld_x, float* out, int64_t ld_out,
@@ -152,7 +158,8 @@ __global__ __launch_bounds__(kBlock) void interact_kernel(TableArgs ta, const fl
     float* S = reinterpret_cast<float*>(lds4);
     const int F = T + 1;
     const int P = F * (F - 1) / 2;
-    float* Zs = S + (size_t)spb * F * D;
+    const int LDR = D + kRowPad;
+    float* Zs = S + (size_t)spb * F * LDR;
     const int tid = threadIdx.x;
     const int lg = tid % G;
     const int g = tid / G;
@@ -164,7 +171,7 @@ __global__ __launch_bounds__(kBlock) void interact_kernel(TableArgs ta, const fl
     for (int e = tid; e < nb * dv; e += kBlock) {
         const int s = e / dv;
         const int d = (e - s * dv) * VEC;
-        V::store(S + (size_t)s * F * D + d, V::load(x + (b0 + s) * ld_x + d));
+        V::store(S + (size_t)s * F * LDR + d, V::load(x + (b0 + s) * ld_x + d));
     }
     // 2. table vectors into S[s][1 + t]
     if constexpr (GATHER) {
@@ -183,7 +190,7 @@ __global__ __launch_bounds__(kBlock) void interact_kernel(TableArgs ta, const fl
                 if (q[u] < 0) continue;
                 const int s = q[u] / T;
                 const int t = q[u] - s * T;
-                float* dst = S + ((size_t)s * F + 1 + t) * D;
+                float* dst = S + ((size_t)s * F + 1 + t) * LDR;
 #pragma unroll
                 for (int c = 0; c < C; ++c) {
                     const int e = (c * G + lg) * VEC;
@@ -198,28 +205,78 @@ __global__ __launch_bounds__(kBlock) void interact_kernel(TableArgs ta, const fl
             const int r = e - s * per;  // element (in VEC units) within the (T, D) block
             const int t = r / dv;
             const int d = (r - t * dv) * VEC;
-            V::store(S + ((size_t)s * F + 1 + t) * D + d, V::load(emb + ((b0 + s) * T + t) * (int64_t)D + d));
+            V::store(S + ((size_t)s * F + 1 + t) * LDR + d, V::load(emb + ((b0 + s) * T + t) * (int64_t)D + d));
         }
     }
     __syncthreads();
 
-    // 3. dots: one flat pair index per lane group at a time
+    // 3. dots
     const int npairs = nb * P;
-    for (int w = g; w < npairs; w += NG) {
-        const int s = w / P;
-        const int p = w - s * P;
-        int i, j;
-        pair_from_flat(p, i, j);
-        const float* si = S + ((size_t)s * F + i) * D;
-        const float* sj = S + ((size_t)s * F + j) * D;
-        float part = 0.f;
+    if constexpr (RT == 0) {
+        // one flat pair index per lane group at a time
+        for (int w = g; w < npairs; w += NG) {
+            const int s = w / P;
+            const int p = w - s * P;
+            int i, j;
+            pair_from_flat(p, i, j);
+            const float* si = S + ((size_t)s * F + i) * LDR;
+            const float* sj = S + ((size_t)s * F + j) * LDR;
+            float part = 0.f;
 #pragma unroll
-        for (int c = 0; c < C; ++c) {
-            const int e = (c * G + lg) * VEC;
-            if (e < D) part = V::dot(V::load(si + e), V::load(sj + e), part);
+            for (int c = 0; c < C; ++c) {
+                const int e = (c * G + lg) * VEC;
+                if (e < D) part = V::dot(V::load(si + e), V::load(sj + e), part);
+            }
+            const float tot = group_sum<G>(part);
+            if (lg == 0) Zs[w] = tot;
         }
-        const float tot = group_sum<G>(part);
-        if (lg == 0) Zs[w] = tot;
+    } else {
+        // RT x RT blocks: rows i = 1 + RT*I + a, columns j = RT*J + b, J <= I;
+        // block number q = I(I+1)/2 + J, decoded as the pair (I+1, J).
+        const int NI = (F - 1 + RT - 1) / RT;
+        const int nblk = NI * (NI + 1) / 2;
+        for (int w = tid; w < nb * nblk; w += kBlock) {
+            const int s = w / nblk;
+            const int q = w - s * nblk;
+            int I1, J;
+            pair_from_flat(q, I1, J);
+            const int i0 = 1 + RT * (I1 - 1);
+            const int j0 = RT * J;
+            const float* Sb = S + (size_t)s * F * LDR;
+            const float* ri[RT];
+            const float* rj[RT];
+#pragma unroll
+            for (int a = 0; a < RT; ++a) {
+                ri[a] = Sb + min(i0 + a, F - 1) * LDR;   // rows past the end are read but never stored
+                rj[a] = Sb + min(j0 + a, F - 1) * LDR;
+            }
+            float acc[RT][RT];
+#pragma unroll
+            for (int a = 0; a < RT; ++a)
+#pragma unroll
+                for (int b = 0; b < RT; ++b) acc[a][b] = 0.f;
+            for (int d = 0; d < D; d += VEC) {
+                typename V::T u[RT], v[RT];
+#pragma unroll
+                for (int a = 0; a < RT; ++a) {
+                    u[a] = V::load(ri[a] + d);
+                    v[a] = V::load(rj[a] + d);
+                }
+#pragma unroll
+                for (int a = 0; a < RT; ++a)
+#pragma unroll
+                    for (int b = 0; b < RT; ++b) acc[a][b] = V::dot(u[a], v[b], acc[a][b]);
+            }
+#pragma unroll
+            for (int a = 0; a < RT; ++a) {
+                const int i = i0 + a;
+#pragma unroll
+                for (int b = 0; b < RT; ++b) {
+                    const int j = j0 + b;
+                    if (i < F && j < i) Zs[s * P + i * (i - 1) / 2 + j] = acc[a][b];
+                }
+            }
+        }
     }
     __syncthreads();
 
@@ -233,7 +290,7 @@ __global__ __launch_bounds__(kBlock) void interact_kernel(TableArgs ta, const fl
         for (int e = tid; e < nb * D; e += kBlock) {
             const int s = e / D;
             const int d = e - s * D;
-            out[(b0 + s) * ld_out + col_x + d] = S[(size_t)s * F * D + d];
+            out[(b0 + s) * ld_out + col_x + d] = S[(size_t)s * F * LDR + d];
         }
     }
 }
@@ -309,14 +366,13 @@ static hipError_t launch_embbag_t(const TableArgs& ta, int T, int D, int64_t B, 
     return hipGetLastError();
 }
 
-template <int VEC, int G, int C, int U, int R, bool GATHER>
+template <int VEC, int G, int C, int U, int R, bool GATHER, int RT>
 static hipError_t launch_interact_t(const TableArgs& ta, const float* emb, int T, int D, int64_t B, int spb,
                                     const float* x, int64_t ld_x, float* out, int64_t ld_out, int col_x, int col_z,
                                     hipStream_t s) {
-    const int F = T + 1, P = F * (F - 1) / 2;
-    const size_t lds = sizeof(float) * ((size_t)spb * F * D + (size_t)spb * P);
+    const size_t lds = interact_lds_bytes(T, D, spb);
     const int64_t blocks = (B + spb - 1) / spb;
-    hipLaunchKernelGGL((interact_kernel<VEC, G, C, U, R, GATHER>), dim3((unsigned)blocks), dim3(kBlock), lds, s, ta,
+    hipLaunchKernelGGL((interact_kernel<VEC, G, C, U, R, GATHER, RT>), dim3((unsigned)blocks), dim3(kBlock), lds, s, ta,
                        emb, T, D, B, spb, x, ld_x, out, ld_out, col_x, col_z);
     return hipGetLastError();
 }
@@ -361,7 +417,7 @@ hipError_t launch_embbag_sum(const TableArgs& ta, int T, int D, int64_t B, bool 
 
 int interact_samples_per_block(int T, int D, int64_t B) {
     const int F = T + 1, P = F * (F - 1) / 2;
-    const size_t per = sizeof(float) * ((size_t)F * D + P);
+    const size_t per = sizeof(float) * ((size_t)F * (D + kRowPad) + P);
     int spb = (int)(kInteractLdsBudget / per);
     if (spb < 1) spb = 1;
     if (spb > 16) spb = 16;
@@ -373,7 +429,7 @@ int interact_samples_per_block(int T, int D, int64_t B) {
 
 size_t interact_lds_bytes(int T, int D, int spb) {
     const int F = T + 1, P = F * (F - 1) / 2;
-    return sizeof(float) * ((size_t)spb * F * D + (size_t)spb * P);
+    return sizeof(float) * ((size_t)spb * F * (D + kRowPad) + (size_t)spb * P);
 }
 
 hipError_t launch_interact(const TableArgs* ta, const float* emb, int T, int D, int64_t B, bool aligned16,
@@ -385,13 +441,20 @@ hipError_t launch_interact(const TableArgs* ta, const float* emb, int T, int D, 
     TableArgs dummy{};
     const TableArgs& t = ta ? *ta : dummy;
     const bool gather = (ta != nullptr);
-#define CALL_I(V, G, C)                                                                                         \
-    if (!gather) return launch_interact_t<V, G, C, 1, 1, false>(t, emb, T, D, B, spb, x, ld_x, out, ld_out,     \
-                                                                col_x, col_z, s);                              \
-    if (multi_hot) return launch_interact_t<V, G, C, 4, 4, true>(t, emb, T, D, B, spb, x, ld_x, out, ld_out,   \
-                                                                 col_x, col_z, s);                             \
-    return launch_interact_t<V, G, C, 8, 1, true>(t, emb, T, D, B, spb, x, ld_x, out, ld_out, col_x, col_z, s);
+#define CALL_I2(V, G, C, RT)                                                                                   \
+    if (!gather) return launch_interact_t<V, G, C, 1, 1, false, RT>(t, emb, T, D, B, spb, x, ld_x, out, ld_out, \
+                                                                    col_x, col_z, s);                          \
+    if (multi_hot) return launch_interact_t<V, G, C, 4, 4, true, RT>(t, emb, T, D, B, spb, x, ld_x, out, ld_out, \
+                                                                     col_x, col_z, s);                         \
+    return launch_interact_t<V, G, C, 8, 1, true, RT>(t, emb, T, D, B, spb, x, ld_x, out, ld_out, col_x, col_z, s);
+#define CALL_I(V, G, C)          \
+    if (T + 1 <= 12) {           \
+        CALL_I2(V, G, C, 0)      \
+    } else {                     \
+        CALL_I2(V, G, C, 4)      \
+    }
     DLRM_DISPATCH_ROW(rs, CALL_I);
+#undef CALL_I2
 #undef CALL_I
 }
 
