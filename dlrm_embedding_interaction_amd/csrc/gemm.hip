@@ -13,9 +13,12 @@
 // each lane reads one float4 of A and one of B from LDS and feeds their
 // four components to four MFMAs (lane l supplies A[l%16][k] and B[k][l%16]
 // with k = 4*(l/16) + q for MFMA q, a permutation of the k order that both
-// operands share).  The next k tile is prefetched into registers while the
-// current one is multiplied.  Bias and activation are applied to the
-// accumulators before the single store.  Block order is remapped so that the
+// operands share).  Two LDS buffers alternate between k tiles and two
+// register stages hold the next two tiles in flight: while tile c is
+// multiplied from one buffer, tile c+1 (fetched one tile earlier) is stored to
+// the other and tile c+3 is requested, so each k tile costs one barrier and
+// global latency is covered by two tiles of MFMA work.  Bias and activation
+// are applied to the accumulators before the single store.  Block order is remapped so that the
 // blocks one XCD runs (the hardware deals blocks to the 8 XCDs round-robin)
 // cover consecutive tiles and share their rows of x in that XCD's L2.
 #include "dlrm_device.h"
@@ -49,8 +52,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bias_act_kernel(int M, int N
     static_assert((VA ? A_V * 4 : A_V) * NT == BM * BK, "A tile must split evenly");
     static_assert((VB ? B_V * 4 : B_V) * NT == BN * BK, "B tile must split evenly");
 
-    __shared__ __attribute__((aligned(16))) float As[BM * LDK];
-    __shared__ __attribute__((aligned(16))) float Bs[BN * LDK];
+    __shared__ __attribute__((aligned(16))) float Abuf[2][BM * LDK];
+    __shared__ __attribute__((aligned(16))) float Bbuf[2][BN * LDK];
 
     const int nblk = tiles_m * tiles_n;
     int bid = blockIdx.x;
@@ -72,12 +75,20 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bias_act_kernel(int M, int N
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    floatx4 ra4[VA ? A_V : 1];
-    float ra1[VA ? 1 : A_V];
-    floatx4 rb4[VB ? B_V : 1];
-    float rb1[VB ? 1 : B_V];
+    // one register stage: this thread's share of an A tile and a B tile
+    struct Stage {
+        floatx4 ra4[VA ? A_V : 1];
+        float ra1[VA ? 1 : A_V];
+        floatx4 rb4[VB ? B_V : 1];
+        float rb1[VB ? 1 : B_V];
+    };
+    Stage st0, st1;
 
-    auto load_tiles = [&](int k0) {
+    auto load_tiles = [&](int k0, Stage& S_) {
+        floatx4* ra4 = S_.ra4;
+        float* ra1 = S_.ra1;
+        floatx4* rb4 = S_.rb4;
+        float* rb1 = S_.rb1;
         if constexpr (VA) {
 #pragma unroll
             for (int i = 0; i < A_V; ++i) {
@@ -139,7 +150,11 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bias_act_kernel(int M, int N
             }
         }
     };
-    auto store_tiles = [&]() {
+    auto store_tiles = [&](const Stage& S_, float* As, float* Bs) {
+        const floatx4* ra4 = S_.ra4;
+        const float* ra1 = S_.ra1;
+        const floatx4* rb4 = S_.rb4;
+        const float* rb1 = S_.rb1;
         if constexpr (VA) {
 #pragma unroll
             for (int i = 0; i < A_V; ++i) {
@@ -179,11 +194,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bias_act_kernel(int M, int N
     const int arow0 = wm * TM * 16 + lrow;
     const int brow0 = wn * TN * 16 + lrow;
 
-    load_tiles(0);
-    for (int k0 = 0; k0 < K; k0 += BK) {
-        store_tiles();
-        __syncthreads();
-        if (k0 + BK < K) load_tiles(k0 + BK);
+    auto multiply = [&](const float* As, const float* Bs) {
 #pragma unroll
         for (int kk = 0; kk < BK; kk += 16) {
             floatx4 af[TM], bf[TN];
@@ -200,6 +211,28 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bias_act_kernel(int M, int N
 #pragma unroll
                     for (int j = 0; j < TN; ++j)
                         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[i][q], bf[j][q], acc[i][j], 0, 0, 0);
+        }
+    };
+
+    // tiles 0 and 1 in flight; tile 0 staged into buffer 0, tile 2 requested
+    load_tiles(0, st0);
+    if (BK < K) load_tiles(BK, st1);
+    store_tiles(st0, Abuf[0], Bbuf[0]);
+    if (2 * BK < K) load_tiles(2 * BK, st0);
+    __syncthreads();
+    // two k tiles per trip so that the register stage of each tile is fixed
+    for (int k0 = 0; k0 < K; k0 += 2 * BK) {
+        multiply(Abuf[0], Bbuf[0]);
+        if (k0 + BK < K) {
+            store_tiles(st1, Abuf[1], Bbuf[1]);
+            if (k0 + 3 * BK < K) load_tiles(k0 + 3 * BK, st1);
+        }
+        __syncthreads();
+        if (k0 + BK >= K) break;
+        multiply(Abuf[1], Bbuf[1]);
+        if (k0 + 2 * BK < K) {
+            store_tiles(st0, Abuf[0], Bbuf[0]);
+            if (k0 + 4 * BK < K) load_tiles(k0 + 4 * BK, st0);
         }
         __syncthreads();
     }
@@ -286,13 +319,11 @@ hipError_t launch_linear(int64_t M, int64_t N, int64_t K, const float* x, int64_
     const int m = (int)M, n = (int)N, k = (int)K;
     // Tile choice measured on MI355X (inside HIP graphs) for the DLRM layer
     // shapes: batches too small to give every CU four 64x64 tiles run best on
-    // 32x32 tiles (one 16x16 MFMA block per wave); short K and mid-size
-    // batches on 64x64; large batches on 128x128 once there are >= 4 per CU.
+    // 32x32 tiles (one 16x16 MFMA block per wave), everything else on 64x64
+    // tiles (a 32x32 sub-tile per wave).
     const int64_t t64 = ((M + 63) / 64) * ((N + 63) / 64);
-    const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
     if (t64 < 1024) return launch_gemm_v<32, 32, 32, 2, 2>(va, vb, m, n, k, x, ld_x, W, bias, act, y, ld_y, s);
-    if (K <= 96 || t128 < 1024) return launch_gemm_v<64, 64, 32, 2, 2>(va, vb, m, n, k, x, ld_x, W, bias, act, y, ld_y, s);
-    return launch_gemm_v<128, 128, 32, 2, 2>(va, vb, m, n, k, x, ld_x, W, bias, act, y, ld_y, s);
+    return launch_gemm_v<64, 64, 32, 2, 2>(va, vb, m, n, k, x, ld_x, W, bias, act, y, ld_y, s);
 }
 
 }  // namespace dlrm
