@@ -39,7 +39,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bias_act_kernel(int M, int N
                                                                     int64_t lda, const float* __restrict__ W,
                                                                     const float* __restrict__ bias, int act,
                                                                     float* __restrict__ Y, int64_t ldy, int tiles_m,
-                                                                    int tiles_n) {
+                                                                    int tiles_n, bool vec_y) {
     constexpr int NT = WM * WN * 64;
     constexpr int TM = BM / (WM * 16);
     constexpr int TN = BN / (WN * 16);
@@ -52,8 +52,12 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bias_act_kernel(int M, int N
     static_assert((VA ? A_V * 4 : A_V) * NT == BM * BK, "A tile must split evenly");
     static_assert((VB ? B_V * 4 : B_V) * NT == BN * BK, "B tile must split evenly");
 
-    __shared__ __attribute__((aligned(16))) float Abuf[2][BM * LDK];
-    __shared__ __attribute__((aligned(16))) float Bbuf[2][BN * LDK];
+    // two A buffers, two B buffers; reused at the end to stage the output tile
+    constexpr int LDC = BN + 4;
+    static_assert(BM * LDC <= 2 * (BM + BN) * LDK, "output tile must fit the tile buffers");
+    __shared__ __attribute__((aligned(16))) float smem[2 * (BM + BN) * LDK];
+    float* const Abuf[2] = {smem, smem + BM * LDK};
+    float* const Bbuf[2] = {smem + 2 * BM * LDK, smem + 2 * BM * LDK + BN * LDK};
 
     const int nblk = tiles_m * tiles_n;
     int bid = blockIdx.x;
@@ -238,18 +242,50 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bias_act_kernel(int M, int N
     }
 
     // Accumulator layout of the 16x16 block: lane l, element r holds
-    // row 4*(l/16) + r, column l%16.
+    // row 4*(l/16) + r, column l%16.  Bias and activation are applied there;
+    // the finished tile is staged in LDS (the loop above ended with a
+    // barrier) and written back row by row, 16 bytes per lane when Y allows.
+    float* const Ct = smem;
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-        const int n = n0 + wn * TN * 16 + j * 16 + (lane & 15);
+        const int cl = wn * TN * 16 + j * 16 + (lane & 15);
+        const int n = n0 + cl;
         const float bv = (bias != nullptr && n < N) ? bias[n] : 0.f;
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int m = m0 + wm * TM * 16 + i * 16 + (lane >> 4) * 4 + r;
-                if (m < M && n < N) Y[(int64_t)m * ldy + n] = apply_act(acc[i][j][r] + bv, act);
+                const int rl = wm * TM * 16 + i * 16 + (lane >> 4) * 4 + r;
+                Ct[rl * LDC + cl] = apply_act(acc[i][j][r] + bv, act);
             }
+        }
+    }
+    __syncthreads();
+    if (vec_y) {
+        constexpr int C4 = BN / 4;
+        for (int f = tid; f < BM * C4; f += NT) {
+            const int rl = f / C4;
+            const int c = (f - rl * C4) * 4;
+            const int m = m0 + rl;
+            const int n = n0 + c;
+            if (m >= M || n >= N) continue;
+            const floatx4 v = *reinterpret_cast<const floatx4*>(&Ct[rl * LDC + c]);
+            float* dst = Y + (int64_t)m * ldy + n;
+            if (n + 3 < N) {
+                *reinterpret_cast<floatx4*>(dst) = v;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (n + e < N) dst[e] = v[e];
+            }
+        }
+    } else {
+        for (int f = tid; f < BM * BN; f += NT) {
+            const int rl = f / BN;
+            const int c = f - rl * BN;
+            const int m = m0 + rl;
+            const int n = n0 + c;
+            if (m < M && n < N) Y[(int64_t)m * ldy + n] = Ct[rl * LDC + c];
         }
     }
 }
@@ -287,7 +323,8 @@ static hipError_t launch_gemm_t(int M, int N, int K, const float* x, int64_t ld_
     const int tm = (M + BM - 1) / BM;
     const int tn = (N + BN - 1) / BN;
     hipLaunchKernelGGL((gemm_bias_act_kernel<BM, BN, BK, WM, WN, VA, VB>), dim3((unsigned)(tm * tn)),
-                       dim3(WM * WN * 64), 0, s, M, N, K, x, ld_x, W, bias, act, y, ld_y, tm, tn);
+                       dim3(WM * WN * 64), 0, s, M, N, K, x, ld_x, W, bias, act, y, ld_y, tm, tn,
+                       (ld_y % 4 == 0) && (((uintptr_t)y & 15u) == 0));
     return hipGetLastError();
 }
 
