@@ -90,6 +90,9 @@ class Oracle:
         L.oracle_embbag_sum.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
                                         ctypes.POINTER(_fp), _i64p, ctypes.POINTER(_i64p), _i64p,
                                         ctypes.POINTER(_i64p), _dp]
+        L.oracle_embbag_ex.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.POINTER(_fp), _i64p,
+                                       ctypes.POINTER(_i64p), _i64p, ctypes.POINTER(_i64p), ctypes.c_int32,
+                                       ctypes.c_int32, _i64p, ctypes.POINTER(_fp), _dp]
         L.oracle_interact.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _dp, ctypes.c_int64,
                                       _dp, _dp, ctypes.c_int64]
         L.oracle_gram.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _dp, ctypes.c_int64,
@@ -97,7 +100,7 @@ class Oracle:
         L.oracle_validate.argtypes = [ctypes.POINTER(_Model), ctypes.c_int64]
         L.oracle_forward.argtypes = [ctypes.POINTER(_Model), ctypes.c_int64, _fp, ctypes.POINTER(_i64p),
                                      _i64p, ctypes.POINTER(_i64p), _dp, _dp, _dp, _dp]
-        for f in ("oracle_pair_closed_form", "oracle_linear", "oracle_embbag_sum", "oracle_interact",
+        for f in ("oracle_pair_closed_form", "oracle_linear", "oracle_embbag_sum", "oracle_embbag_ex", "oracle_interact",
                   "oracle_gram", "oracle_validate", "oracle_forward"):
             getattr(L, f).restype = ctypes.c_int
 
@@ -156,6 +159,34 @@ class Oracle:
         out = np.empty((B, T, D), np.float64)
         rc = self._L.oracle_embbag_sum(T, B, D, W, rows, I, N, O, out.ctypes.data_as(_dp))
         self._check(rc, "embbag_sum")
+        return out
+
+    MODES = {"sum": 0, "mean": 1, "max": 2}
+
+    def embbag_ex(self, tables, indices, offsets, mode="sum", include_last_offset=False, padding_idx=None,
+                  per_sample_weights=None) -> np.ndarray:
+        """General bags: mode sum / mean / max, optional per-sample weights (sum only),
+        include_last_offset, per-table padding index (None or -1: none).  Indices and
+        offsets may be int32 or int64; they are widened to int64 exactly."""
+        T = len(tables)
+        widen = lambda a: np.ascontiguousarray(a.detach().cpu().numpy() if hasattr(a, "detach") else a).astype(np.int64)
+        keep, W, rows, I, N, O = self._tables(tables, [widen(i) for i in indices], [widen(o) for o in offsets])
+        D = keep[0][0].shape[1]
+        B = keep[2][0].shape[0] - (1 if include_last_offset else 0)
+        out = np.empty((max(B, 0), T, D), np.float64)
+        pad = None
+        if padding_idx is not None:
+            pads = padding_idx if isinstance(padding_idx, (list, tuple)) else [padding_idx] * T
+            pad = (ctypes.c_int64 * T)(*[(-1 if p is None else int(p)) for p in pads])
+        psw = None
+        keep_w = None
+        if per_sample_weights is not None:
+            keep_w = [_np(w, np.float32) for w in per_sample_weights]
+            psw = (_fp * T)(*[w.ctypes.data_as(_fp) for w in keep_w])
+        rc = self._L.oracle_embbag_ex(T, B, D, W, rows, I, N, O, self.MODES[mode], int(bool(include_last_offset)),
+                                      ctypes.cast(pad, _i64p) if pad is not None else None, psw,
+                                      out.ctypes.data_as(_dp))
+        self._check(rc, "embbag_ex")
         return out
 
     def interact(self, x, E) -> np.ndarray:

@@ -171,6 +171,68 @@ int oracle_embbag_sum(int32_t T, int64_t B, int32_t D, const float* const* W, co
     return ORACLE_OK;
 }
 
+/*
+ * General embedding bags (the reduce_op form of the same LessonsLearned entry,
+ * point 2: output[b] = reduce_op(weight[indices[offsets[b]:offsets[b+1]]]),
+ * with the arguments that movement.rs translate_embedding_bag and
+ * dlrm_pattern.rs match_dlrm name: mode, per_sample_weights,
+ * include_last_offset, padding_idx).  Definitions, per PyTorch's
+ * nn.EmbeddingBag which those arguments come from:
+ *   mode 0 (sum):  sum over the bag of w_k * row(idx_k)   (w_k = 1 without weights)
+ *   mode 1 (mean): sum of the rows / number of rows        (empty bag: 0)
+ *   mode 2 (max):  elementwise maximum of the rows          (empty bag: 0)
+ *   include_last_offset: off has B + 1 entries and bag b ends at off[b + 1];
+ *     otherwise off has B entries and the last bag ends at n_idx.
+ *   padding_idx pad[t] >= 0: indices equal to it are left out of the bag
+ *     (not summed, not counted, not maxed).
+ * psw: per-sample weights per table (n_idx[t] values) or NULL; sum mode only.
+ */
+int oracle_embbag_ex(int32_t T, int64_t B, int32_t D, const float* const* W, const int64_t* rows,
+                     const int64_t* const* idx, const int64_t* n_idx, const int64_t* const* off,
+                     int32_t mode, int32_t include_last_offset, const int64_t* pad,
+                     const float* const* psw, double* out) {
+    if (T < 1 || B < 0 || D < 1 || mode < 0 || mode > 2) return ORACLE_E_SHAPE;
+    if (!W || !rows || !idx || !n_idx || !off || (B > 0 && !out)) return ORACLE_E_NULL;
+    if (psw && mode != 0) return ORACLE_E_SHAPE;
+    for (int32_t t = 0; t < T; ++t) {
+        if (!W[t] || !off[t] || (n_idx[t] > 0 && !idx[t]) || (psw && n_idx[t] > 0 && !psw[t])) return ORACLE_E_NULL;
+        if (rows[t] < 1 || n_idx[t] < 0) return ORACLE_E_SHAPE;
+        for (int64_t b = 0; b < B; ++b) {
+            int64_t s = off[t][b];
+            int64_t e = include_last_offset ? off[t][b + 1] : ((b + 1 < B) ? off[t][b + 1] : n_idx[t]);
+            if (s < 0 || s > e || e > n_idx[t]) return ORACLE_E_INDEX;
+        }
+        for (int64_t k = 0; k < n_idx[t]; ++k)
+            if (idx[t][k] < 0 || idx[t][k] >= rows[t]) return ORACLE_E_INDEX;
+    }
+    int64_t b;
+#pragma omp parallel for schedule(static)
+    for (b = 0; b < B; ++b) {
+        for (int32_t t = 0; t < T; ++t) {
+            const int64_t s = off[t][b];
+            const int64_t e = include_last_offset ? off[t][b + 1] : ((b + 1 < B) ? off[t][b + 1] : n_idx[t]);
+            double* o = out + (b * T + t) * (int64_t)D;
+            int64_t count = 0;
+            for (int32_t d = 0; d < D; ++d) o[d] = 0.0;
+            for (int64_t k = s; k < e; ++k) {
+                const int64_t r = idx[t][k];
+                if (pad && pad[t] >= 0 && r == pad[t]) continue;
+                const float* row = W[t] + r * (int64_t)D;
+                const double w = psw ? (double)psw[t][k] : 1.0;
+                for (int32_t d = 0; d < D; ++d) {
+                    const double v = (double)row[d];
+                    if (mode == 2) o[d] = (count == 0 || v > o[d]) ? v : o[d];
+                    else o[d] += w * v;
+                }
+                ++count;
+            }
+            if (mode == 1 && count > 0)
+                for (int32_t d = 0; d < D; ++d) o[d] /= (double)count;
+        }
+    }
+    return ORACLE_OK;
+}
+
 /* Feature vector f of sample b: f = 0 is x[b], f = t+1 is E[b][t]. */
 static const double* feature(const double* x, int64_t ldx, const double* E, int32_t T, int32_t D,
                              int64_t b, int32_t f) {

@@ -113,6 +113,99 @@ def pin_embbag_rejects_malformed(o):
             raise AssertionError("malformed bag input accepted")
 
 
+def _ragged_case(seed, T=3, B=23, D=6, V=30, max_len=6, with_pad=True):
+    r = _rng(seed)
+    tables, idx, off = [], [], []
+    for t in range(T):
+        o, n = di.ragged_bags(B, max_len, seed * 10 + t, empty_frac=0.25)
+        tables.append(r.standard_normal((V, D)).astype(np.float32))
+        ix = r.integers(0, V, n).astype(np.int64)
+        if with_pad and n:
+            ix[r.random(n) < 0.2] = 3          # padding index 3 appears often
+        idx.append(ix)
+        off.append(o.numpy())
+    return tables, idx, off
+
+
+def pin_embbag_ex_matches_torch_embedding_bag(o):
+    """mode sum / mean / max, per-sample weights, include_last_offset and padding_idx
+    against torch.nn.functional.embedding_bag in fp64 (the general bag of the
+    LessonsLearned 'EmbeddingBag translator gap' entry, whose follow-ups these are)."""
+    F_ = torch.nn.functional
+    for mode in ("sum", "mean", "max"):
+        for last in (False, True):
+            for pad in (None, 3):
+                for weighted in ((False, True) if mode == "sum" else (False,)):
+                    tables, idx, off = _ragged_case(11 + len(mode) + 2 * last + 3 * (pad is not None) + 5 * weighted)
+                    r = _rng(99)
+                    psw = [r.standard_normal(i.shape[0]).astype(np.float32) for i in idx] if weighted else None
+                    offs = [np.concatenate([ob, [ix.shape[0]]]) for ob, ix in zip(off, idx)] if last else off
+                    got = o.embbag_ex(tables, idx, offs, mode=mode, include_last_offset=last, padding_idx=pad,
+                                      per_sample_weights=psw)
+                    for t in range(len(tables)):
+                        ref = F_.embedding_bag(torch.from_numpy(idx[t]), torch.from_numpy(tables[t]).double(),
+                                               torch.from_numpy(offs[t]), mode=mode,
+                                               per_sample_weights=(torch.from_numpy(psw[t]).double() if weighted
+                                                                   else None),
+                                               include_last_offset=last, padding_idx=pad).numpy()
+                        np.testing.assert_allclose(got[:, t, :], ref, rtol=1e-12, atol=1e-12,
+                                                   err_msg=f"{mode} last={last} pad={pad} w={weighted}")
+
+
+def pin_embbag_ex_brute_force_integer(o):
+    """Integer tables: max is exact, sum exact, mean = exact sum / count; brute force in int64."""
+    r = _rng(12)
+    T, B, D, V = 2, 17, 5, 40
+    tables_i = [r.integers(-8, 9, (V, D)).astype(np.int64) for _ in range(T)]
+    idx, off = [], []
+    for t in range(T):
+        o_, n = di.ragged_bags(B, 7, 700 + t)
+        idx.append(r.integers(0, V, n).astype(np.int64))
+        off.append(o_.numpy())
+    tf = [t.astype(np.float32) for t in tables_i]
+    for mode in ("sum", "mean", "max"):
+        got = o.embbag_ex(tf, idx, off, mode=mode, padding_idx=[5, None])
+        for t in range(T):
+            ends = list(off[t][1:]) + [idx[t].shape[0]]
+            for b in range(B):
+                ks = [k for k in range(off[t][b], ends[b]) if not (t == 0 and idx[t][k] == 5)]
+                rows_ = [tables_i[t][idx[t][k]] for k in ks]
+                if not rows_:
+                    want = np.zeros(D)
+                elif mode == "sum":
+                    want = np.sum(rows_, 0).astype(np.float64)
+                elif mode == "mean":
+                    want = np.sum(rows_, 0).astype(np.float64) / len(rows_)
+                else:
+                    want = np.max(rows_, 0).astype(np.float64)
+                assert np.array_equal(got[b, t], want), (mode, t, b)
+
+
+def pin_embbag_ex_last_offset_is_a_slice_end(o):
+    """With include_last_offset the last bag is indices[off[B-1]:off[B]] (the pages'
+    offsets[b]:offsets[b+1] slice); a final offset short of the index count leaves
+    the trailing indices out.  Brute force with numpy slicing."""
+    r = _rng(14)
+    D, V, B = 3, 20, 6
+    tab = r.standard_normal((V, D)).astype(np.float32)
+    idx = r.integers(0, V, 15).astype(np.int64)
+    off = np.array([0, 2, 2, 5, 9, 11, 12], np.int64)          # B + 1 entries, 12 < 15
+    got = o.embbag_ex([tab], [idx], [off], mode="sum", include_last_offset=True)
+    for b in range(B):
+        want = tab[idx[off[b]:off[b + 1]]].astype(np.float64).sum(0) if off[b + 1] > off[b] else np.zeros(D)
+        np.testing.assert_allclose(got[b, 0], want, rtol=1e-13, atol=1e-13)
+
+
+def pin_embbag_ex_int32_equals_int64(o):
+    """The same bags addressed with int32 indices and offsets give the same result."""
+    tables, idx, off = _ragged_case(13, with_pad=False)
+    a = o.embbag_ex(tables, idx, off, mode="mean")
+    b = o.embbag_ex(tables, [i.astype(np.int32) for i in idx], [x.astype(np.int32) for x in off], mode="mean")
+    assert np.array_equal(a, b)
+    # and sum mode without options is the plain bag sum
+    assert np.array_equal(o.embbag_ex(tables, idx, off), o.embbag_sum(tables, idx, off))
+
+
 # --- interaction --------------------------------------------------------------
 
 

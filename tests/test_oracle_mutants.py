@@ -15,7 +15,8 @@ import pins
 MUTANTS = {
     "embbag_keeps_last_row_only": [("o[d] += (double)row[d];", "o[d] = (double)row[d];")],
     "embbag_last_bag_empty": [("*e = (b + 1 < B) ? off[b + 1] : n_idx;", "*e = (b + 1 < B) ? off[b + 1] : off[b];")],
-    "embbag_skips_first_index": [("for (int64_t k = s; k < e; ++k) {", "for (int64_t k = s + (e > s); k < e; ++k) {")],
+    "embbag_skips_first_index": [("for (int64_t k = s; k < e; ++k) {\n                const float* row = W[t] + idx[t][k]",
+                                  "for (int64_t k = s + (e > s); k < e; ++k) {\n                const float* row = W[t] + idx[t][k]")],
     "interact_squares_left_vector": [("acc += u[d] * v[d];\n                Z", "acc += u[d] * u[d];\n                Z")],
     "interact_reversed_pair_order": [("Z[b * ldz + p] = acc;", "Z[b * ldz + (P - 1 - p)] = acc;")],
     "interact_drops_last_feature": [("for (int32_t i = 1; i < F; ++i) {\n            for (int32_t j = 0; j < i; ++j) {\n                const double* u",
@@ -31,6 +32,13 @@ MUTANTS = {
                       ("h1[b * wr + D + p] = Z[b * P + p];", "h1[b * wr + p] = Z[b * P + p];")],
     "top_last_layer_relu": [("last ? ORACLE_ACT_SIGMOID : ORACLE_ACT_RELU", "ORACLE_ACT_RELU")],
     "validate_ignores_pair_count": [("if (m->ln_top[0] != m->D + oracle_n_pairs(m->T + 1)) return ORACLE_E_SHAPE;", "")],
+    "bag_mean_counts_padding": [("if (pad && pad[t] >= 0 && r == pad[t]) continue;",
+                                 "if (pad && pad[t] >= 0 && r == pad[t]) { ++count; continue; }")],
+    "bag_max_keeps_first_row": [("if (mode == 2) o[d] = (count == 0 || v > o[d]) ? v : o[d];",
+                                 "if (mode == 2) o[d] = (count == 0) ? v : o[d];")],
+    "bag_ignores_sample_weights": [("const double w = psw ? (double)psw[t][k] : 1.0;", "const double w = 1.0;")],
+    "bag_ignores_last_offset": [("            const int64_t e = include_last_offset ? off[t][b + 1] : ((b + 1 < B) ? off[t][b + 1] : n_idx[t]);",
+                                 "            const int64_t e = (b + 1 < B) ? off[t][b + 1] : n_idx[t];")],
     "pair_count_off_by_one": [("return n_feat * (n_feat - 1) / 2;", "return n_feat * (n_feat + 1) / 2 - n_feat + (n_feat > 40);")],
 }
 
