@@ -40,6 +40,14 @@ class DlrmError(RuntimeError):
         self.code = code
 
 
+class _BagOptions(ctypes.Structure):
+    _fields_ = [("mode", ctypes.c_int32), ("include_last_offset", ctypes.c_int32), ("index_bytes", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("padding_idx", _i64p), ("per_sample_weights", ctypes.POINTER(_vp))]
+
+
+BAG_MODES = {"sum": 0, "mean": 1, "max": 2}
+
+
 class _Model(ctypes.Structure):
     _fields_ = [
         ("n_bot", ctypes.c_int32), ("ln_bot", _i64p),
@@ -76,6 +84,8 @@ def load(build_if_missing: bool = True) -> ctypes.CDLL:
     L.dlrm_abi_version.restype = ctypes.c_int32
     L.dlrm_embbag_sum.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.POINTER(_vp), _i64p,
                                   ctypes.POINTER(_vp), _i64p, ctypes.POINTER(_vp), _vp, _vp]
+    L.dlrm_embbag.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.POINTER(_vp), _i64p,
+                              ctypes.POINTER(_vp), _i64p, ctypes.POINTER(_vp), ctypes.POINTER(_BagOptions), _vp, _vp]
     L.dlrm_interact_lower_tri.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _vp, ctypes.c_int64,
                                           _vp, _vp, ctypes.c_int64, ctypes.c_int32, _vp]
     L.dlrm_embbag_interact.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.POINTER(_vp), _i64p,
@@ -90,7 +100,7 @@ def load(build_if_missing: bool = True) -> ctypes.CDLL:
     L.dlrm_embbag_check_indices.argtypes = [ctypes.c_int32, ctypes.c_int64, _i64p, ctypes.POINTER(_vp), _i64p,
                                             ctypes.POINTER(_vp), _vp, _vp]
     L.dlrm_pair_index_map.argtypes = [ctypes.c_int32, _vp, _vp, _vp]
-    for f in ("dlrm_embbag_sum", "dlrm_interact_lower_tri", "dlrm_embbag_interact", "dlrm_linear_bias_act", "dlrm_forward",
+    for f in ("dlrm_embbag_sum", "dlrm_embbag", "dlrm_interact_lower_tri", "dlrm_embbag_interact", "dlrm_linear_bias_act", "dlrm_forward",
               "dlrm_embbag_check_indices", "dlrm_pair_index_map"):
         getattr(L, f).restype = ctypes.c_int
     if L.dlrm_abi_version() != ABI_VERSION:
@@ -151,6 +161,53 @@ def embbag_sum(tables: List[torch.Tensor], indices: List[torch.Tensor], offsets:
     rc = L.dlrm_embbag_sum(T, B, D, _ptrs(tables), _i64s([t.shape[0] for t in tables]), _ptrs(indices),
                            _i64s([i.numel() for i in indices]), _ptrs(offsets), out.data_ptr(), _stream(out.device))
     _check(rc, "dlrm_embbag_sum")
+    return out
+
+
+def embbag(tables: List[torch.Tensor], indices: List[torch.Tensor], offsets: List[torch.Tensor],
+           mode: str = "sum", include_last_offset: bool = False, padding_idx=None,
+           per_sample_weights: Optional[List[torch.Tensor]] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """General bags of every table in one launch -> (B, T, D) fp32.
+
+    mode 'sum' | 'mean' | 'max'; per_sample_weights (sum only) one fp32 tensor
+    per table; include_last_offset: offsets hold B + 1 entries; padding_idx an
+    int or one int / None per table.  Indices and offsets are all int64 or all
+    int32."""
+    L = load()
+    T = len(tables)
+    if not (T == len(indices) == len(offsets)) or T == 0:
+        raise ValueError("tables, indices and offsets must have the same non-zero length")
+    itype = indices[0].dtype
+    if itype not in (torch.int32, torch.int64):
+        raise TypeError("indices must be int32 or int64")
+    for i, t in enumerate(tables):
+        _dev(t, torch.float32, f"tables[{i}]")
+        _dev(indices[i], itype, f"indices[{i}]")
+        _dev(offsets[i], itype, f"offsets[{i}]")
+    D = tables[0].shape[1]
+    B = offsets[0].shape[0] - (1 if include_last_offset else 0)
+    if out is None:
+        out = torch.empty((B, T, D), device=tables[0].device, dtype=torch.float32)
+    _dev(out, torch.float32, "out")
+    if tuple(out.shape) != (B, T, D) or any(t.shape[1] != D for t in tables):
+        raise ValueError("shape mismatch")
+    opts = _BagOptions(BAG_MODES[mode], int(bool(include_last_offset)), 4 if itype == torch.int32 else 8, 0)
+    keep = []
+    if padding_idx is not None:
+        pads = padding_idx if isinstance(padding_idx, (list, tuple)) else [padding_idx] * T
+        arr = _i64s([-1 if p is None else int(p) for p in pads])
+        keep.append(arr)
+        opts.padding_idx = ctypes.cast(arr, _i64p)
+    if per_sample_weights is not None:
+        for i, w in enumerate(per_sample_weights):
+            _dev(w, torch.float32, f"per_sample_weights[{i}]")
+        arr = _ptrs(per_sample_weights)
+        keep.append(arr)
+        opts.per_sample_weights = ctypes.cast(arr, ctypes.POINTER(_vp))
+    rc = L.dlrm_embbag(T, B, D, _ptrs(tables), _i64s([t.shape[0] for t in tables]), _ptrs(indices),
+                       _i64s([i.numel() for i in indices]), _ptrs(offsets), ctypes.byref(opts), out.data_ptr(),
+                       _stream(out.device))
+    _check(rc, "dlrm_embbag")
     return out
 
 

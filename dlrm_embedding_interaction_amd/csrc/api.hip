@@ -119,6 +119,39 @@ DLRM_API dlrm_status_t dlrm_embbag_sum(int32_t num_tables, int64_t batch, int32_
     return from_hip(launch_embbag_sum(ta, num_tables, dim, batch, aligned, multi_hot, out, (hipStream_t)stream));
 }
 
+DLRM_API dlrm_status_t dlrm_embbag(int32_t num_tables, int64_t batch, int32_t dim, const float* const* weights,
+                                   const int64_t* rows, const void* const* indices, const int64_t* n_indices,
+                                   const void* const* offsets, const dlrm_bag_options_t* opts, float* out,
+                                   void* stream) {
+    if (!weights || !rows || !indices || !n_indices || !offsets || !opts || !out) return DLRM_E_NULL;
+    if (num_tables < 1 || batch < 1 || dim < 1) return DLRM_E_SHAPE;
+    if (num_tables > DLRM_MAX_TABLES || dim > kMaxDim || batch > kIntLimit) return DLRM_E_UNSUPPORTED;
+    if (opts->mode < DLRM_BAG_SUM || opts->mode > DLRM_BAG_MAX) return DLRM_E_SHAPE;
+    if (opts->index_bytes != 4 && opts->index_bytes != 8) return DLRM_E_SHAPE;
+    if (opts->per_sample_weights && opts->mode != DLRM_BAG_SUM) return DLRM_E_SHAPE;
+    BagArgs ba;
+    memset(&ba, 0, sizeof(ba));
+    bool al = (dim % 4 == 0) && al16(out);
+    bool mh = false;
+    for (int32_t t = 0; t < num_tables; ++t) {
+        if (!weights[t] || !offsets[t]) return DLRM_E_NULL;
+        if (rows[t] < 1 || n_indices[t] < 0 || n_indices[t] > kIntLimit * 64) return DLRM_E_SHAPE;
+        if (opts->index_bytes == 4 && n_indices[t] > INT32_MAX) return DLRM_E_UNSUPPORTED;
+        if (n_indices[t] > 0 && !indices[t]) return DLRM_E_NULL;
+        if (opts->per_sample_weights && n_indices[t] > 0 && !opts->per_sample_weights[t]) return DLRM_E_NULL;
+        ba.w[t] = weights[t];
+        ba.idx[t] = indices[t];
+        ba.off[t] = offsets[t];
+        ba.nidx[t] = n_indices[t];
+        ba.psw[t] = opts->per_sample_weights ? opts->per_sample_weights[t] : nullptr;
+        ba.pad[t] = (opts->padding_idx && opts->padding_idx[t] >= 0) ? opts->padding_idx[t] : -1;
+        al = al && al16(weights[t]);
+        mh = mh || (n_indices[t] > batch);
+    }
+    return from_hip(launch_embbag_ex(ba, num_tables, dim, batch, opts->mode, opts->include_last_offset ? 1 : 0,
+                                     opts->index_bytes == 4, al, mh, out, (hipStream_t)stream));
+}
+
 DLRM_API dlrm_status_t dlrm_interact_lower_tri(int64_t batch, int32_t num_tables, int32_t dim, const float* x,
                                                int64_t ld_x, const float* emb, float* out, int64_t ld_out,
                                                int32_t concat_dense, void* stream) {

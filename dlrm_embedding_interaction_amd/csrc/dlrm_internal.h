@@ -23,6 +23,16 @@ struct CheckArgs {
     int64_t rows[DLRM_MAX_TABLES];
 };
 
+// Arguments of the general bag kernel (3 KiB of kernel arguments).
+struct BagArgs {
+    const float* w[DLRM_MAX_TABLES];
+    const void* idx[DLRM_MAX_TABLES];     // int32 or int64, per the launch
+    const void* off[DLRM_MAX_TABLES];
+    int64_t nidx[DLRM_MAX_TABLES];
+    const float* psw[DLRM_MAX_TABLES];    // per-sample weights or NULL
+    int64_t pad[DLRM_MAX_TABLES];         // padding index or -1
+};
+
 bool row_shape_supported(int D);
 int interact_samples_per_block(int T, int D, int64_t B);
 size_t interact_lds_bytes(int T, int D, int spb);
@@ -39,6 +49,10 @@ hipError_t launch_embbag_sum(const TableArgs& ta, int T, int D, int64_t B, bool 
 hipError_t launch_interact(const TableArgs* ta, const float* emb, int T, int D, int64_t B, bool aligned16,
                            bool multi_hot, const float* x, int64_t ld_x, float* out, int64_t ld_out, int col_x,
                            int col_z, hipStream_t s);
+
+// General bags (mode, weights, include_last_offset, padding) into out (B, T, D).
+hipError_t launch_embbag_ex(const BagArgs& ba, int T, int D, int64_t B, int mode, int last_off, bool idx32,
+                            bool aligned16, bool multi_hot, float* out, hipStream_t s);
 
 hipError_t launch_check_indices(const CheckArgs& ca, int T, int64_t B, int32_t* bad, hipStream_t s);
 

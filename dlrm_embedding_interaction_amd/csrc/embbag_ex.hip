@@ -1,0 +1,146 @@
+// embbag_ex.hip -- general multi-table embedding bags on gfx950: sum, mean or
+// max pooling, optional per-sample weights, include_last_offset, a padding
+// index per table, and 32- or 64-bit indices and offsets.
+//
+// Definition (LessonsLearned entry "DLRM compile: EmbeddingBag translator
+// gap", point 2, on "luminal compare dlrm-fused-kernels...dlrm-pt2-megakernel":
+// output[b] = reduce_op(weight[indices[offsets[b]:offsets[b+1]]]), with the
+// argument set that movement.rs translate_embedding_bag reads there: mode,
+// per_sample_weights, include_last_offset, padding_idx):
+//   sum   sum of w_k * row(idx_k), w_k = 1 without weights
+//   mean  sum of the rows / number of rows (empty bag: 0)
+//   max   elementwise maximum of the rows (empty bag: 0)
+// Indices equal to the table's padding index are left out of the bag.  With
+// include_last_offset the offsets hold B + 1 entries and bag b ends at
+// offsets[b + 1]; otherwise the last bag ends at the index count.
+//
+// Same layout as the plain bag kernel: one row per group of G lanes, 16 bytes
+// per lane, U bags per group in flight, R row indices fetched per step.  The
+// mode is a uniform run-time branch; the index width is a template argument.
+#include "dlrm_device.h"
+#include "dlrm_internal.h"
+#include "rowvec.h"
+
+namespace dlrm {
+
+template <int VEC, int G, int C, int U, int R, typename IDX>
+__global__ __launch_bounds__(kBlock) void embbag_ex_kernel(BagArgs ba, int T, int D, int64_t B, int mode,
+                                                           int last_off, float* __restrict__ out) {
+    using V = Vec<VEC>;
+    constexpr int NG = kBlock / G;
+    const int lg = threadIdx.x % G;
+    const int g = threadIdx.x / G;
+    const int64_t nbags = B * T;
+    const int64_t base = (int64_t)blockIdx.x * NG * U;
+
+    const float* wp[U];
+    const IDX* ip[U];
+    const float* ps[U];
+    int64_t pad[U];
+    int len[U], cnt[U];
+    int64_t q[U];
+    typename V::T acc[U][C];
+    const typename V::T init = (mode == DLRM_BAG_MAX) ? V::splat(-INFINITY) : V::zero();
+    int maxlen = 0;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        q[u] = base + u * NG + g;
+        len[u] = 0;
+        cnt[u] = 0;
+        wp[u] = nullptr;
+        ip[u] = nullptr;
+        ps[u] = nullptr;
+        pad[u] = -1;
+        if (q[u] < nbags) {
+            const int64_t b = q[u] / T;
+            const int t = (int)(q[u] - b * T);
+            const IDX* off = reinterpret_cast<const IDX*>(ba.off[t]);
+            const int64_t s = (int64_t)off[b];
+            const int64_t e = last_off ? (int64_t)off[b + 1] : ((b + 1 < B) ? (int64_t)off[b + 1] : ba.nidx[t]);
+            len[u] = (int)(e - s);
+            wp[u] = ba.w[t];
+            ip[u] = reinterpret_cast<const IDX*>(ba.idx[t]) + s;
+            ps[u] = ba.psw[t] ? ba.psw[t] + s : nullptr;
+            pad[u] = ba.pad[t];
+        }
+        maxlen = max(maxlen, len[u]);
+#pragma unroll
+        for (int c = 0; c < C; ++c) acc[u][c] = init;
+    }
+    for (int r0 = 0; r0 < maxlen; r0 += R) {
+        int64_t row[R][U];
+        float wt[R][U];
+#pragma unroll
+        for (int rr = 0; rr < R; ++rr)
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const bool in = r0 + rr < len[u];
+                const int64_t r = in ? (int64_t)ip[u][r0 + rr] : -1;
+                row[rr][u] = (r == pad[u]) ? -1 : r;     // padding rows leave the bag
+                wt[rr][u] = (in && ps[u]) ? ps[u][r0 + rr] : 1.f;
+            }
+        typename V::T v[R][U][C];
+#pragma unroll
+        for (int rr = 0; rr < R; ++rr)
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int c = 0; c < C; ++c) {
+                    const int e = (c * G + lg) * VEC;
+                    v[rr][u][c] = (row[rr][u] >= 0 && e < D) ? V::load(wp[u] + row[rr][u] * D + e) : V::zero();
+                }
+#pragma unroll
+        for (int rr = 0; rr < R; ++rr)
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (row[rr][u] >= 0) {
+                    ++cnt[u];
+#pragma unroll
+                    for (int c = 0; c < C; ++c) {
+                        if (mode == DLRM_BAG_MAX) acc[u][c] = V::max(acc[u][c], v[rr][u][c]);
+                        else if (ps[u]) acc[u][c] = V::fma(wt[rr][u], v[rr][u][c], acc[u][c]);
+                        else acc[u][c] = V::add(acc[u][c], v[rr][u][c]);
+                    }
+                }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        if (q[u] >= nbags) continue;
+        float* o = out + q[u] * (int64_t)D;
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            const int e = (c * G + lg) * VEC;
+            if (e >= D) continue;
+            typename V::T r = acc[u][c];
+            if (cnt[u] == 0) r = V::zero();
+            else if (mode == DLRM_BAG_MEAN) r = V::div(r, (float)cnt[u]);
+            V::store(o + e, r);
+        }
+    }
+}
+
+template <int VEC, int G, int C, int U, int R, typename IDX>
+static hipError_t launch_ex_t(const BagArgs& ba, int T, int D, int64_t B, int mode, int last_off, float* out,
+                              hipStream_t s) {
+    constexpr int NG = kBlock / G;
+    const int64_t blocks = (B * T + (int64_t)NG * U - 1) / ((int64_t)NG * U);
+    hipLaunchKernelGGL((embbag_ex_kernel<VEC, G, C, U, R, IDX>), dim3((unsigned)blocks), dim3(kBlock), 0, s, ba, T,
+                       D, B, mode, last_off, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_embbag_ex(const BagArgs& ba, int T, int D, int64_t B, int mode, int last_off, bool idx32,
+                            bool aligned16, bool multi_hot, float* out, hipStream_t s) {
+    const RowShape rs = row_shape(D, aligned16);
+#define CALL_EX(V, G, C)                                                                                   \
+    if (idx32) {                                                                                           \
+        if (multi_hot) return launch_ex_t<V, G, C, 4, 4, int32_t>(ba, T, D, B, mode, last_off, out, s);    \
+        return launch_ex_t<V, G, C, 8, 1, int32_t>(ba, T, D, B, mode, last_off, out, s);                  \
+    }                                                                                                      \
+    if (multi_hot) return launch_ex_t<V, G, C, 4, 4, int64_t>(ba, T, D, B, mode, last_off, out, s);        \
+    return launch_ex_t<V, G, C, 8, 1, int64_t>(ba, T, D, B, mode, last_off, out, s);
+    DLRM_DISPATCH_ROW(rs, CALL_EX);
+#undef CALL_EX
+}
+
+}  // namespace dlrm

@@ -126,6 +126,53 @@ dlrm_status_t dlrm_embbag_sum(int32_t num_tables, int64_t batch, int32_t dim,
                               const int64_t* const* indices, const int64_t* n_indices,
                               const int64_t* const* offsets, float* out, void* stream);
 
+/* Pooling modes of dlrm_embbag. */
+#define DLRM_BAG_SUM 0
+#define DLRM_BAG_MEAN 1
+#define DLRM_BAG_MAX 2
+
+/*
+ * Options of dlrm_embbag: the arguments of PyTorch's embedding_bag that the
+ * pages' translator names and leaves to follow-up work (movement.rs
+ * translate_embedding_bag and dlrm_pattern.rs match_dlrm on "luminal compare
+ * dlrm-fused-kernels...dlrm-pt2-megakernel").
+ *   mode                 DLRM_BAG_SUM, DLRM_BAG_MEAN or DLRM_BAG_MAX
+ *   include_last_offset  0: offsets[t] hold batch entries, the last bag ends at
+ *                        n_indices[t]; 1: offsets[t] hold batch + 1 entries and
+ *                        bag b is [offsets[t][b], offsets[t][b+1])
+ *   index_bytes          8: indices and offsets are int64; 4: int32
+ *   padding_idx          host[T] or NULL; entry p >= 0 leaves the indices equal
+ *                        to p out of every bag of table t (-1: none)
+ *   per_sample_weights   host[T] of device pointers to n_indices[t] fp32
+ *                        weights, or NULL; sum mode only
+ */
+typedef struct dlrm_bag_options {
+    int32_t mode;
+    int32_t include_last_offset;
+    int32_t index_bytes;
+    int32_t reserved;
+    const int64_t* padding_idx;
+    const float* const* per_sample_weights;
+} dlrm_bag_options_t;
+
+/*
+ * dlrm_embbag -- general embedding bags of T tables in one launch:
+ * out[b][t] = reduce(weights[t][i] for the indices i of bag b), with
+ * reduce = sum (times the per-sample weight), mean (the sum over the number of
+ * indices in the bag) or elementwise max; an empty bag gives zeros.  Source:
+ * the reduce_op form of the bag on the LessonsLearned entry "DLRM compile:
+ * EmbeddingBag translator gap", point 2, "luminal compare
+ * dlrm-fused-kernels...dlrm-pt2-megakernel".
+ * Arguments as dlrm_embbag_sum, except that indices and offsets are untyped
+ * device pointers of the width opts->index_bytes gives, and opts may not be
+ * NULL.  Sums accumulate in fp32 in increasing k; the mean divides the fp32
+ * sum by the count.
+ */
+dlrm_status_t dlrm_embbag(int32_t num_tables, int64_t batch, int32_t dim, const float* const* weights,
+                          const int64_t* rows, const void* const* indices, const int64_t* n_indices,
+                          const void* const* offsets, const dlrm_bag_options_t* opts, float* out,
+                          void* stream);
+
 /*
  * dlrm_interact_lower_tri -- pairwise-dot feature interaction.
  *

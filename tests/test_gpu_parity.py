@@ -438,3 +438,80 @@ def test_embbag_interact_in_place_beside_x(orc):
     Z = orc.interact(x.double().numpy(), E)
     mag = orc.interact(x.abs().double().numpy(), np.abs(E))
     assert np.all(np.abs(Rc[:, D:D + P].double().numpy() - Z) <= gamma(D) * mag + 1e-30)
+
+
+# --- general bags: mean / max, weights, include_last_offset, padding, int32 ----------
+
+
+def _general_case(seed, T, B, D, V, max_len, pad_row=3):
+    gen = torch.Generator().manual_seed(seed)
+    tables, idx, off = [], [], []
+    for t in range(T):
+        o, n = di.ragged_bags(B, max_len, seed * 10 + t, empty_frac=0.2)
+        tables.append(torch.randint(-8, 9, (V, D), generator=gen).float())
+        ix = torch.randint(0, V, (n,), generator=gen)
+        if n:
+            ix[torch.rand(n, generator=gen) < 0.2] = pad_row
+        idx.append(ix)
+        off.append(o)
+    return tables, idx, off
+
+
+@pytest.mark.parametrize("mode", ["sum", "mean", "max"])
+@pytest.mark.parametrize("last", [False, True])
+@pytest.mark.parametrize("pad", [None, 3])
+@pytest.mark.parametrize("itype", [torch.int64, torch.int32])
+@pytest.mark.parametrize("D", [6, 64, 128])
+def test_general_bags_integer_tables(mode, last, pad, itype, D, orc):
+    """Integer tables: sum and max bit-exact; mean within one fp32 rounding of the exact quotient."""
+    T, B = 3, 97
+    tables, idx, off = _general_case(31 + D, T, B, D, 50, 24 if D == 128 else 6)
+    offs = [torch.cat([o, torch.tensor([i.numel()])]) for o, i in zip(off, idx)] if last else off
+    got = dl.embbag([t.cuda() for t in tables], [i.to(itype).cuda() for i in idx], [o.to(itype).cuda() for o in offs],
+                    mode=mode, include_last_offset=last, padding_idx=pad)
+    torch.cuda.synchronize()
+    ref = orc.embbag_ex(tables, idx, offs, mode=mode, include_last_offset=last, padding_idx=pad)
+    g = got.cpu().double().numpy()
+    if mode == "mean":
+        assert np.all(np.abs(g - ref) <= U * np.abs(ref))
+    else:
+        assert np.array_equal(g, ref)
+
+
+def test_general_bags_weighted_sum_within_bound(orc):
+    T, B, D = 4, 300, 64
+    tables, idx, off = _general_case(41, T, B, D, 400, 30)
+    gen = torch.Generator().manual_seed(42)
+    tables = [torch.randn(t.shape, generator=gen) for t in tables]
+    psw = [torch.randn(i.numel(), generator=gen) for i in idx]
+    got = dl.embbag([t.cuda() for t in tables], [i.cuda() for i in idx], [o.cuda() for o in off], mode="sum",
+                    padding_idx=[3, None, 3, None], per_sample_weights=[w.cuda() for w in psw])
+    torch.cuda.synchronize()
+    ref = orc.embbag_ex(tables, idx, off, mode="sum", padding_idx=[3, None, 3, None], per_sample_weights=psw)
+    mag = orc.embbag_ex([t.abs() for t in tables], idx, off, mode="sum", padding_idx=[3, None, 3, None],
+                        per_sample_weights=[w.abs() for w in psw])
+    assert np.all(np.abs(got.cpu().double().numpy() - ref) <= gamma(31) * mag + 1e-30)
+
+
+def test_general_bags_float_mean_and_max_stress_shape(orc):
+    """The 26-table, d=128, bag-20 Zipf shape at a reduced batch: max exact, mean within bound."""
+    w = di.custom("general_stress", 2048, 13, 26, 100_000, 128, 20, (13, 128), dist="zipf", cfg_id=17)
+    inp = di.make_inputs(w)
+    g = on_gpu(inp)
+    for mode in ("max", "mean"):
+        got = dl.embbag(g.tables, g.indices, g.offsets, mode=mode).cpu().double().numpy()
+        ref = orc.embbag_ex(inp.tables, inp.indices, inp.offsets, mode=mode)
+        if mode == "max":
+            assert np.array_equal(got, ref)
+        else:
+            mag = orc.embbag_ex([t.abs() for t in inp.tables], inp.indices, inp.offsets, mode="mean")
+            assert np.all(np.abs(got - ref) <= gamma(21) * mag + 1e-30)
+
+
+def test_general_sum_equals_plain_bag_sum():
+    """With no options the general call is the plain bag sum, bit for bit (int64 and int32 indices)."""
+    inp = on_gpu(di.make_inputs(di.custom("gen_plain", 777, 3, 5, 3000, 64, 7, (3, 64), cfg_id=18)))
+    plain = dl.embbag_sum(inp.tables, inp.indices, inp.offsets)
+    g64 = dl.embbag(inp.tables, inp.indices, inp.offsets)
+    g32 = dl.embbag(inp.tables, [i.int() for i in inp.indices], [o.int() for o in inp.offsets])
+    assert torch.equal(plain, g64) and torch.equal(plain, g32)

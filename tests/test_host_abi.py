@@ -135,6 +135,21 @@ def test_embbag_argument_errors(lib):
     assert f(2, 4, 4, p, n, p, neg, p, 4096, None) == dl.DLRM_E_SHAPE
 
 
+def test_general_bag_argument_errors(lib):
+    f = lib.dlrm_embbag
+    p = (dl._vp * 2)(4096, 4096)
+    n = dl._i64s([4, 4])
+    ok = dl._BagOptions(0, 0, 8, 0)
+    assert f(2, 4, 4, p, n, p, n, p, None, 4096, None) == dl.DLRM_E_NULL          # no options
+    assert f(2, 4, 4, p, n, p, n, p, ctypes.byref(dl._BagOptions(3, 0, 8, 0)), 4096, None) == dl.DLRM_E_SHAPE
+    assert f(2, 4, 4, p, n, p, n, p, ctypes.byref(dl._BagOptions(0, 0, 2, 0)), 4096, None) == dl.DLRM_E_SHAPE
+    wts = (dl._vp * 2)(4096, 4096)
+    mean_w = dl._BagOptions(1, 0, 8, 0, None, ctypes.cast(wts, ctypes.POINTER(dl._vp)))
+    assert f(2, 4, 4, p, n, p, n, p, ctypes.byref(mean_w), 4096, None) == dl.DLRM_E_SHAPE   # weights need sum
+    assert f(65, 4, 4, p, n, p, n, p, ctypes.byref(ok), 4096, None) == dl.DLRM_E_UNSUPPORTED
+    assert f(2, 4, 4, p, n, p, n, p, ctypes.byref(ok), None, None) == dl.DLRM_E_NULL
+
+
 def test_interact_argument_errors(lib):
     f = lib.dlrm_interact_lower_tri
     assert f(4, 3, 16, None, 16, 4096, 4096, 22, 1, None) == dl.DLRM_E_NULL
