@@ -135,10 +135,10 @@ hipError_t launch_embbag_ex(const BagArgs& ba, int T, int D, int64_t B, int mode
 #define CALL_EX(V, G, C)                                                                                   \
     if (idx32) {                                                                                           \
         if (multi_hot) return launch_ex_t<V, G, C, 4, 4, int32_t>(ba, T, D, B, mode, last_off, out, s);    \
-        return launch_ex_t<V, G, C, 8, 1, int32_t>(ba, T, D, B, mode, last_off, out, s);                  \
+        return launch_ex_t<V, G, C, 4, 1, int32_t>(ba, T, D, B, mode, last_off, out, s);                  \
     }                                                                                                      \
     if (multi_hot) return launch_ex_t<V, G, C, 4, 4, int64_t>(ba, T, D, B, mode, last_off, out, s);        \
-    return launch_ex_t<V, G, C, 8, 1, int64_t>(ba, T, D, B, mode, last_off, out, s);
+    return launch_ex_t<V, G, C, 4, 1, int64_t>(ba, T, D, B, mode, last_off, out, s);
     DLRM_DISPATCH_ROW(rs, CALL_EX);
 #undef CALL_EX
 }

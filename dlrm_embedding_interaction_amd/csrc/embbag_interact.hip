@@ -27,7 +27,9 @@
 //    vectors each lane owns a 4x4 block of the strict lower triangle (block
 //    index decoded with the same closed form) and accumulates its 16 dots
 //    over d from float4 LDS reads, 8 reads per 64 FMAs and no cross-lane
-//    traffic.  The P results of a sample are staged in LDS and written as
+//    traffic; when that leaves most lanes of a block idle, 2 or 4
+//    neighbouring lanes split d for one block and add their partial blocks
+//    with DPP.  The P results of a sample are staged in LDS and written as
 //    one contiguous row segment.
 #include "dlrm_device.h"
 #include "dlrm_internal.h"
@@ -129,12 +131,13 @@ __global__ __launch_bounds__(kBlock) void embbag_sum_kernel(TableArgs ta, int T,
 
 // ---- interaction, with the bags either gathered (GATHER) or read from E ------
 // LDS: S[spb][F][D + kRowPad] then Zs[spb][P].  RT = 0: lane-group dots;
-// RT = 4: per-lane 4x4 register blocks of the triangle.
+// RT = 4: per-lane 4x4 register blocks of the triangle, d split over dsplit
+// neighbouring lanes.
 template <int VEC, int G, int C, int U, int R, bool GATHER, int RT>
 __global__ __launch_bounds__(kBlock) void interact_kernel(TableArgs ta, const float* __restrict__ emb, int T,
                                                           int D, int64_t B, int spb, const float* x,
                                                           int64_t ld_x, float* out, int64_t ld_out,
-                                                          int col_x, int col_z) {
+                                                          int col_x, int col_z, int dsplit) {
     using V = Vec<VEC>;
     constexpr int NG = kBlock / G;
     extern __shared__ float4 lds4[];
@@ -215,17 +218,22 @@ __global__ __launch_bounds__(kBlock) void interact_kernel(TableArgs ta, const fl
         }
     } else {
         // RT x RT blocks: rows i = 1 + RT*I + a, columns j = RT*J + b, J <= I;
-        // block number q = I(I+1)/2 + J, decoded as the pair (I+1, J).
+        // block number q = I(I+1)/2 + J, decoded as the pair (I+1, J).  With
+        // dsplit > 1, dsplit neighbouring lanes take equal slices of d for the
+        // same block and add their partial blocks with DPP (xor 1, xor 2).
         const int NI = (F - 1 + RT - 1) / RT;
         const int nblk = NI * (NI + 1) / 2;
-        for (int w = tid; w < nb * nblk; w += kBlock) {
-            const int s = w / nblk;
-            const int q = w - s * nblk;
+        const int dlen = D / dsplit;
+        for (int w = tid; w < nb * nblk * dsplit; w += kBlock) {
+            const int wq = w / dsplit;
+            const int h = w - wq * dsplit;
+            const int s = wq / nblk;
+            const int q = wq - s * nblk;
             int I1, J;
             pair_from_flat(q, I1, J);
             const int i0 = 1 + RT * (I1 - 1);
             const int j0 = RT * J;
-            const float* Sb = S + (size_t)s * F * LDR;
+            const float* Sb = S + (size_t)s * F * LDR + h * dlen;
             const float* ri[RT];
             const float* rj[RT];
 #pragma unroll
@@ -238,7 +246,7 @@ __global__ __launch_bounds__(kBlock) void interact_kernel(TableArgs ta, const fl
             for (int a = 0; a < RT; ++a)
 #pragma unroll
                 for (int b = 0; b < RT; ++b) acc[a][b] = 0.f;
-            for (int d = 0; d < D; d += VEC) {
+            for (int d = 0; d < dlen; d += VEC) {
                 typename V::T u[RT], v[RT];
 #pragma unroll
                 for (int a = 0; a < RT; ++a) {
@@ -250,13 +258,24 @@ __global__ __launch_bounds__(kBlock) void interact_kernel(TableArgs ta, const fl
 #pragma unroll
                     for (int b = 0; b < RT; ++b) acc[a][b] = V::dot(u[a], v[b], acc[a][b]);
             }
+            if (dsplit > 1) {
 #pragma unroll
-            for (int a = 0; a < RT; ++a) {
-                const int i = i0 + a;
+                for (int a = 0; a < RT; ++a)
 #pragma unroll
-                for (int b = 0; b < RT; ++b) {
-                    const int j = j0 + b;
-                    if (i < F && j < i) Zs[s * P + i * (i - 1) / 2 + j] = acc[a][b];
+                    for (int b = 0; b < RT; ++b) {
+                        acc[a][b] += dpp_quad_xor1(acc[a][b]);
+                        if (dsplit > 2) acc[a][b] += dpp_quad_xor2(acc[a][b]);
+                    }
+            }
+            if (h == 0) {
+#pragma unroll
+                for (int a = 0; a < RT; ++a) {
+                    const int i = i0 + a;
+#pragma unroll
+                    for (int b = 0; b < RT; ++b) {
+                        const int j = j0 + b;
+                        if (i < F && j < i) Zs[s * P + i * (i - 1) / 2 + j] = acc[a][b];
+                    }
                 }
             }
         }
@@ -327,11 +346,11 @@ static hipError_t launch_embbag_t(const TableArgs& ta, int T, int D, int64_t B, 
 template <int VEC, int G, int C, int U, int R, bool GATHER, int RT>
 static hipError_t launch_interact_t(const TableArgs& ta, const float* emb, int T, int D, int64_t B, int spb,
                                     const float* x, int64_t ld_x, float* out, int64_t ld_out, int col_x, int col_z,
-                                    hipStream_t s) {
+                                    int dsplit, hipStream_t s) {
     const size_t lds = interact_lds_bytes(T, D, spb);
     const int64_t blocks = (B + spb - 1) / spb;
     hipLaunchKernelGGL((interact_kernel<VEC, G, C, U, R, GATHER, RT>), dim3((unsigned)blocks), dim3(kBlock), lds, s, ta,
-                       emb, T, D, B, spb, x, ld_x, out, ld_out, col_x, col_z);
+                       emb, T, D, B, spb, x, ld_x, out, ld_out, col_x, col_z, dsplit);
     return hipGetLastError();
 }
 
@@ -341,7 +360,7 @@ hipError_t launch_embbag_sum(const TableArgs& ta, int T, int D, int64_t B, bool 
     const RowShape rs = row_shape(D, aligned16);
 #define CALL_E(V, G, C)                                                            \
     if (multi_hot) return launch_embbag_t<V, G, C, 4, 4>(ta, T, D, B, out, s);     \
-    return launch_embbag_t<V, G, C, 8, 1>(ta, T, D, B, out, s);
+    return launch_embbag_t<V, G, C, 4, 1>(ta, T, D, B, out, s);
     DLRM_DISPATCH_ROW(rs, CALL_E);
 #undef CALL_E
 }
@@ -368,18 +387,28 @@ hipError_t launch_interact(const TableArgs* ta, const float* emb, int T, int D, 
                            int col_z, hipStream_t s) {
     const RowShape rs = row_shape(D, aligned16);
     const int spb = interact_samples_per_block(T, D, B);
+    // dot layout: lane-group dots for few vectors; otherwise per-lane 4x4
+    // register blocks, with d split over 2 or 4 lanes while that leaves fewer
+    // work items than threads (the slices stay multiples of the vector width)
+    const int F = T + 1;
+    const int n4 = (F - 1 + 3) / 4;
+    const int items = spb * n4 * (n4 + 1) / 2;
+    const int vw = (rs.vec == 4) ? 4 : 1;
+    int dsplit = 1;
+    while (dsplit < 4 && items * dsplit * 2 <= kBlock && D % (vw * dsplit * 2) == 0) dsplit *= 2;
     if (interact_lds_bytes(T, D, spb) > kMaxLdsBytes) return hipErrorInvalidValue;
     TableArgs dummy{};
     const TableArgs& t = ta ? *ta : dummy;
     const bool gather = (ta != nullptr);
 #define CALL_I2(V, G, C, RT)                                                                                   \
     if (!gather) return launch_interact_t<V, G, C, 1, 1, false, RT>(t, emb, T, D, B, spb, x, ld_x, out, ld_out, \
-                                                                    col_x, col_z, s);                          \
+                                                                    col_x, col_z, dsplit, s);                  \
     if (multi_hot) return launch_interact_t<V, G, C, 4, 4, true, RT>(t, emb, T, D, B, spb, x, ld_x, out, ld_out, \
-                                                                     col_x, col_z, s);                         \
-    return launch_interact_t<V, G, C, 8, 1, true, RT>(t, emb, T, D, B, spb, x, ld_x, out, ld_out, col_x, col_z, s);
+                                                                     col_x, col_z, dsplit, s);                 \
+    return launch_interact_t<V, G, C, 4, 1, true, RT>(t, emb, T, D, B, spb, x, ld_x, out, ld_out, col_x, col_z, \
+                                                      dsplit, s);
 #define CALL_I(V, G, C)          \
-    if (T + 1 <= 12) {           \
+    if (F <= 12) {               \
         CALL_I2(V, G, C, 0)      \
     } else {                     \
         CALL_I2(V, G, C, 4)      \
