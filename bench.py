@@ -46,6 +46,8 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--secondary", action="store_true", help="also time the 32-table workload")
     p.add_argument("--kernel-reps", type=int, default=50)
+    p.add_argument("--cold-steps", type=int, default=20,
+                   help="forwards timed one by one after a 1 GiB flush of the caches (0: skip)")
     p.add_argument("--sweep", metavar="OUT_JSON", default=None,
                    help="time every batch x tables cell of the sweep grid, write them to OUT_JSON, print no line")
     p.add_argument("--copy-calibration", action="store_true",
@@ -115,15 +117,27 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "num_tables": w.num_tables, "rows_per_table": w.rows,
                    "dim": w.dim, "bag": w.bag, "ln_bot": list(w.ln_bot), "ln_top": list(w.ln_top),
                    "mode": "eager" if args.eager else "hip_graph", "index_sets": args.index_sets},
+        "us_per_forward_p10_p50_p90": [res["pct"]["p10"], res["pct"]["p50"], res["pct"]["p90"]],
+        "us_per_forward_cold_p50": res["cold_us"],
         "roofline": res["roofline"],
         "roofline_emb_interact": res["roofline_emb"],
         "emb_interact_GBps": res["roofline_emb"]["achieved"],
+        "mlp_TFLOPs": res["mlp_tflops"],
+        "mlp_frac_of_fp32_mfma_peak": res["mlp_tflops"] / FP32_MFMA_PEAK_TFLOPS,
         "kernels": res["kernels"],
     }
+    if not args.copy_calibration:   # counter runs keep the calibration copy the only copy kernel
+        ceiling = copy_ceiling(torch, dev)
+        out["copy_ceiling_GBps"] = ceiling
+        out["roofline_emb_interact"]["frac_of_copy_ceiling"] = out["roofline_emb_interact"]["achieved"] / ceiling
     if args.secondary:
         w2 = di.MANYTABLE
         r2 = run_workload(torch, dl, di, w2, dev, args)
         out["secondary"] = {w2.name: {"us_per_forward": r2["ms_per_step"] * 1e3,
+                                      "us_per_forward_p10_p50_p90": [r2["pct"]["p10"], r2["pct"]["p50"],
+                                                                     r2["pct"]["p90"]],
+                                      "us_per_forward_cold_p50": r2["cold_us"],
+                                      "mlp_TFLOPs": r2["mlp_tflops"],
                                       "samples_per_s": r2["samples_per_s"],
                                       "emb_interact_GBps": r2["roofline_emb"]["achieved"],
                                       "roofline": r2["roofline"], "roofline_emb_interact": r2["roofline_emb"]}}
@@ -181,13 +195,44 @@ def run_workload(torch, dl, di, w, dev, args):
     t1 = time.perf_counter()
     ms = (t1 - t0) * 1e3 / args.steps
 
+    # per-step distribution: the same replays, each between two events
+    n_pct = min(args.steps, 200)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_pct)]
+    for i, (a, b) in enumerate(evs):
+        a.record()
+        run(i)
+        b.record()
+    torch.cuda.synchronize()
+    per = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
+    pct = {"p10": per[len(per) // 10], "p50": per[len(per) // 2], "p90": per[(len(per) * 9) // 10]}
+
+    # cold caches: a 1 GiB read-modify-write between forwards evicts L2 and the Infinity Cache
+    cold = None
+    if args.cold_steps > 0:
+        flush = torch.empty(1 << 28, device=dev)
+        flush.zero_()
+        ct = []
+        for i in range(args.cold_steps):
+            flush.add_(1.0)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            run(i)
+            b.record()
+            ct.append((a, b))
+        torch.cuda.synchronize()
+        cold = sorted(a.elapsed_time(b) * 1e3 for a, b in ct)[len(ct) // 2]
+        del flush
+
     kernels = time_stages(torch, dl, model, inp, idx_sets, ws, w, args.kernel_reps)
     traffic = counted_traffic(w.name)
     roof = roofline(kernels, dominant=True, traffic=traffic)
     roof_emb = roofline([k for k in kernels if k["name"] == "emb_interact"], dominant=True, traffic=traffic)
     del inp, model, idx_sets, ws, argsets
     torch.cuda.empty_cache()
-    return dict(ms_per_step=ms, samples_per_s=B / (ms * 1e-3), kernels=kernels, roofline=roof, roofline_emb=roof_emb)
+    mlp = [k for k in kernels if k["name"] != "emb_interact"]
+    mlp_tf = sum(k["flops"] for k in mlp) / (sum(k["us"] for k in mlp) * 1e-6) / 1e12
+    return dict(ms_per_step=ms, samples_per_s=B / (ms * 1e-3), kernels=kernels, roofline=roof, roofline_emb=roof_emb,
+                pct=pct, cold_us=cold, mlp_tflops=mlp_tf)
 
 
 def time_stages(torch, dl, model, inp, idx_sets, ws, w, reps):
@@ -302,6 +347,24 @@ def roofline(kernels, dominant=True, traffic=None):
     return {"kernel": k["name"], "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS, "traffic": tr, "us_per_launch": k["us"],
             "bytes_per_launch": k["bytes"]}
+
+
+def copy_ceiling(torch, dev, nbytes=1 << 30, reps=10):
+    """Read + write GB/s of a plain 1 GiB device-to-device copy (torch's copy kernel)."""
+    a = torch.ones(nbytes // 4, device=dev)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    gbps = 2 * nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del a, b
+    return gbps
 
 
 def copy_calibration(torch, dev, nbytes=512 << 20, reps=5):

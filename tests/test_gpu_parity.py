@@ -515,3 +515,28 @@ def test_general_sum_equals_plain_bag_sum():
     g64 = dl.embbag(inp.tables, inp.indices, inp.offsets)
     g32 = dl.embbag(inp.tables, [i.int() for i in inp.indices], [o.int() for o in inp.offsets])
     assert torch.equal(plain, g64) and torch.equal(plain, g32)
+
+
+def test_stacked_table_layout_is_bit_identical():
+    """One (sum V_t, D) allocation addressed through per-table row ranges (the
+    stacked layout) gives the same bags and forward as separate tables."""
+    w = di.custom("stacked", 513, 13, 6, 7000, 64, 2, (13, 64), hidden_top=(64,), cfg_id=19)
+    inp = on_gpu(di.make_inputs(w))
+    stacked = torch.cat(inp.tables, 0)
+    views = [stacked[t * w.rows:(t + 1) * w.rows] for t in range(w.num_tables)]
+    assert views[1].data_ptr() == stacked.data_ptr() + w.rows * w.dim * 4
+    a = dl.embbag_sum(inp.tables, inp.indices, inp.offsets)
+    b = dl.embbag_sum(views, inp.indices, inp.offsets)
+    assert torch.equal(a, b)
+    fa = dl.Model.from_inputs(inp).forward(inp.dense, inp.indices, inp.offsets).clone()
+    sv = di.Inputs(w, inp.dense, views, inp.indices, inp.offsets, inp.bot_w, inp.bot_b, inp.top_w, inp.top_b)
+    fb = dl.Model.from_inputs(sv).forward(inp.dense, inp.indices, inp.offsets)
+    assert torch.equal(fa, fb)
+
+
+@pytest.mark.parametrize("T,D", [(64, 64), (2, 1024), (40, 33)])
+def test_forward_at_the_size_limits(T, D, orc):
+    """Most tables (64, so F = 65 and P = 2080), the longest rows (1024) and odd widths."""
+    w = di.custom(f"limits_{T}_{D}", 64, 5, T, 300, D, 1, (5, 16, D), hidden_top=(32,), cfg_id=20)
+    inp = di.make_inputs(w)
+    _forward_check(inp, on_gpu(inp), orc)
