@@ -42,6 +42,8 @@ def parse():
     p.add_argument("--workload", default="page4")
     p.add_argument("--index-sets", type=int, default=8)
     p.add_argument("--eager", action="store_true", help="time plain calls instead of graph replays")
+    p.add_argument("--path", default="auto", choices=["auto", "fused", "layered"],
+                   help="dlrm_forward (auto), dlrm_forward_fused or dlrm_forward_layered")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--secondary", action="store_true", help="also time the 32-table workload")
@@ -116,7 +118,8 @@ def main():
         "data": f"synthetic (seeded; dense U[0,1), tables N(0,1/D), {w.dist} indices, bag {w.bag})",
         "config": {"workload": w.name, "batch": w.batch, "num_tables": w.num_tables, "rows_per_table": w.rows,
                    "dim": w.dim, "bag": w.bag, "ln_bot": list(w.ln_bot), "ln_top": list(w.ln_top),
-                   "mode": "eager" if args.eager else "hip_graph", "index_sets": args.index_sets},
+                   "mode": "eager" if args.eager else "hip_graph", "index_sets": args.index_sets,
+                   "path": args.path},
         "us_per_forward_p10_p50_p90": [res["pct"]["p10"], res["pct"]["p50"], res["pct"]["p90"]],
         "us_per_forward_cold_p50": res["cold_us"],
         "roofline": res["roofline"],
@@ -161,7 +164,8 @@ def run_workload(torch, dl, di, w, dev, args):
     argsets = [model.forward_args(inp.dense, idx, inp.offsets) for idx in idx_sets]
 
     def step(i):
-        model.forward(inp.dense, idx_sets[i % nsets], inp.offsets, out=out, workspace=ws, args=argsets[i % nsets])
+        model.forward(inp.dense, idx_sets[i % nsets], inp.offsets, out=out, workspace=ws, args=argsets[i % nsets],
+                      path=args.path)
 
     for i in range(nsets):
         step(i)

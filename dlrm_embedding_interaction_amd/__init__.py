@@ -28,7 +28,7 @@ LIBRARY = os.path.join(HERE, "libdlrm_mi355x.so")
 DLRM_OK, DLRM_E_NULL, DLRM_E_SHAPE, DLRM_E_WORKSPACE, DLRM_E_UNSUPPORTED, DLRM_E_HIP, DLRM_E_INDEX = range(7)
 ACT_NONE, ACT_RELU, ACT_SIGMOID = 0, 1, 2
 MAX_TABLES = 64
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 _i64p = ctypes.POINTER(ctypes.c_int64)
 _vp = ctypes.c_void_p
@@ -57,6 +57,7 @@ class _Model(ctypes.Structure):
         ("emb_w", ctypes.POINTER(_vp)),
         ("bot_w", ctypes.POINTER(_vp)), ("bot_b", ctypes.POINTER(_vp)),
         ("top_w", ctypes.POINTER(_vp)), ("top_b", ctypes.POINTER(_vp)),
+        ("packed_w", _vp),
     ]
 
 
@@ -97,11 +98,17 @@ def load(build_if_missing: bool = True) -> ctypes.CDLL:
     L.dlrm_forward_workspace_bytes.restype = ctypes.c_size_t
     L.dlrm_forward.argtypes = [ctypes.POINTER(_Model), ctypes.c_int64, _vp, ctypes.POINTER(_vp), _i64p,
                                ctypes.POINTER(_vp), _vp, _vp, ctypes.c_size_t, _vp]
+    L.dlrm_forward_layered.argtypes = L.dlrm_forward.argtypes
+    L.dlrm_pack_weights_bytes.argtypes = [ctypes.POINTER(_Model)]
+    L.dlrm_pack_weights_bytes.restype = ctypes.c_size_t
+    L.dlrm_pack_weights.argtypes = [ctypes.POINTER(_Model), _vp, ctypes.c_size_t, _vp]
+    L.dlrm_forward_fused.argtypes = [ctypes.POINTER(_Model), ctypes.c_int64, _vp, ctypes.POINTER(_vp), _i64p,
+                                     ctypes.POINTER(_vp), _vp, _vp]
     L.dlrm_embbag_check_indices.argtypes = [ctypes.c_int32, ctypes.c_int64, _i64p, ctypes.POINTER(_vp), _i64p,
                                             ctypes.POINTER(_vp), _vp, _vp]
     L.dlrm_pair_index_map.argtypes = [ctypes.c_int32, _vp, _vp, _vp]
     for f in ("dlrm_embbag_sum", "dlrm_embbag", "dlrm_interact_lower_tri", "dlrm_embbag_interact", "dlrm_linear_bias_act", "dlrm_forward",
-              "dlrm_embbag_check_indices", "dlrm_pair_index_map"):
+              "dlrm_forward_layered", "dlrm_forward_fused", "dlrm_pack_weights", "dlrm_embbag_check_indices", "dlrm_pair_index_map"):
         getattr(L, f).restype = ctypes.c_int
     if L.dlrm_abi_version() != ABI_VERSION:
         raise ImportError(f"{LIBRARY}: ABI version {L.dlrm_abi_version()} != {ABI_VERSION}")
@@ -291,6 +298,9 @@ def linear_bias_act(x: torch.Tensor, W: torch.Tensor, bias: Optional[torch.Tenso
     return out
 
 
+FORWARD_PATHS = {"auto": "dlrm_forward", "fused": "dlrm_forward_fused", "layered": "dlrm_forward_layered"}
+
+
 class Model:
     """DLRMv1 parameters resident on one GPU, with the fused ``forward``.
 
@@ -299,8 +309,8 @@ class Model:
     the library is built once; tensors are kept alive by this object.
     """
 
-    def __init__(self, tables, bot_w, bot_b, top_w, top_b, n_dense: Optional[int] = None):
-        load()
+    def __init__(self, tables, bot_w, bot_b, top_w, top_b, n_dense: Optional[int] = None, pack: bool = True):
+        L = load()
         self.tables = [_dev(t, torch.float32, "table") for t in tables]
         self.bot_w = [_dev(w, torch.float32, "bot_w") for w in bot_w]
         self.bot_b = [_dev(b, torch.float32, "bot_b") for b in bot_b]
@@ -316,8 +326,28 @@ class Model:
                       _ptrs(self.tables), _ptrs(self.bot_w), _ptrs(self.bot_b), _ptrs(self.top_w), _ptrs(self.top_b))
         lb, lt, rows, emb, bw, bb, tw, tb = self._keep
         self._desc = _Model(len(self.ln_bot), ctypes.cast(lb, _i64p), len(self.ln_top), ctypes.cast(lt, _i64p),
-                            self.num_tables, self.dim, ctypes.cast(rows, _i64p), emb, bw, bb, tw, tb)
+                            self.num_tables, self.dim, ctypes.cast(rows, _i64p), emb, bw, bb, tw, tb, None)
         self._ws: Optional[torch.Tensor] = None
+        # weights packed once for the single-launch forward (when the model fits it)
+        self.packed: Optional[torch.Tensor] = None
+        if pack:
+            self.repack()
+
+    def repack(self) -> bool:
+        """(Re)write the packed weights of the single-launch forward from the
+        current Linear weights; False when the model is outside that path."""
+        L = load()
+        self._desc.packed_w = None
+        n = int(L.dlrm_pack_weights_bytes(ctypes.byref(self._desc)))
+        if n == 0:
+            self.packed = None
+            return False
+        if self.packed is None or self.packed.numel() * 4 < n:
+            self.packed = torch.empty((n + 3) // 4, dtype=torch.float32, device=self.device)
+        _check(L.dlrm_pack_weights(ctypes.byref(self._desc), self.packed.data_ptr(), n, _stream(self.device)),
+               "dlrm_pack_weights")
+        self._desc.packed_w = self.packed.data_ptr()
+        return True
 
     @classmethod
     def from_inputs(cls, inp) -> "Model":
@@ -342,7 +372,11 @@ class Model:
 
     def forward(self, dense: torch.Tensor, indices: List[torch.Tensor], offsets: List[torch.Tensor],
                 out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                args=None) -> torch.Tensor:
+                args=None, path: str = "auto") -> torch.Tensor:
+        """The whole forward.  ``path``: "auto" (dlrm_forward: the library picks),
+        "fused" (dlrm_forward_fused, one launch) or "layered" (dlrm_forward_layered)."""
+        if path not in FORWARD_PATHS:
+            raise ValueError(f"path must be one of {sorted(FORWARD_PATHS)}")
         L = load()
         _dev(dense, torch.float32, "dense")
         if len(indices) != self.num_tables or len(offsets) != self.num_tables:
@@ -358,13 +392,19 @@ class Model:
         _dev(out, torch.float32, "out")
         if out.numel() != B:
             raise ValueError("out must hold B values")
-        ws = workspace if workspace is not None else self.workspace(B)
         if args is None:
             args = self.forward_args(dense, indices, offsets)
         b, dp, ip, nn_, op = args
-        rc = L.dlrm_forward(ctypes.byref(self._desc), b, dp, ip, nn_, op, out.data_ptr(), ws.data_ptr(),
+        if path == "fused":
+            rc = L.dlrm_forward_fused(ctypes.byref(self._desc), b, dp, ip, nn_, op, out.data_ptr(),
+                                      _stream(self.device))
+            _check(rc, "dlrm_forward_fused")
+            return out
+        ws = workspace if workspace is not None else self.workspace(B)
+        fn = FORWARD_PATHS[path]
+        rc = getattr(L, fn)(ctypes.byref(self._desc), b, dp, ip, nn_, op, out.data_ptr(), ws.data_ptr(),
                             ws.numel() * ws.element_size(), _stream(self.device))
-        _check(rc, "dlrm_forward")
+        _check(rc, fn)
         return out
 
 

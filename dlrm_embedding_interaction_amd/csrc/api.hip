@@ -204,10 +204,12 @@ DLRM_API size_t dlrm_forward_workspace_bytes(const dlrm_model_t* m, int64_t batc
     return p.total;
 }
 
-DLRM_API dlrm_status_t dlrm_forward(const dlrm_model_t* m, int64_t batch, const float* dense,
-                                    const int64_t* const* indices, const int64_t* n_indices,
-                                    const int64_t* const* offsets, float* out, void* workspace, size_t ws_bytes,
-                                    void* stream) {
+namespace {
+
+// Checks shared by every forward entry point; fills the table arguments.
+dlrm_status_t forward_args(const dlrm_model_t* m, int64_t batch, const float* dense, const int64_t* const* indices,
+                           const int64_t* n_indices, const int64_t* const* offsets, const float* out,
+                           TableArgs& ta, bool* aligned, bool* multi_hot) {
     dlrm_status_t st = validate_model(m, batch);
     if (st != DLRM_OK) return st;
     if (!dense || !indices || !n_indices || !offsets || !out) return DLRM_E_NULL;
@@ -216,16 +218,84 @@ DLRM_API dlrm_status_t dlrm_forward(const dlrm_model_t* m, int64_t batch, const 
         if (!m->bot_w[l] || !m->bot_b[l]) return DLRM_E_NULL;
     for (int32_t l = 0; l + 1 < m->n_top; ++l)
         if (!m->top_w[l] || !m->top_b[l]) return DLRM_E_NULL;
-    const int32_t T = m->num_tables, D = m->emb_dim;
+    return fill_tables(ta, m->num_tables, batch, m->emb_dim, m->emb_w, m->rows, indices, n_indices, offsets, aligned,
+                       multi_hot);
+}
+
+// Kernel arguments of the single-launch path (with packed-weight pointers
+// relative to `packed`, which may be NULL when only the shape is checked);
+// false when the model is outside its limits.
+bool fused_args(const dlrm_model_t* m, int64_t batch, const float* dense, float* out, const TableArgs& ta,
+                bool aligned, const float* packed, FusedArgs& fa) {
+    if (m->n_bot - 1 > kFusedMaxLayers || m->n_top - 1 > kFusedMaxLayers) return false;
+    memset(&fa, 0, sizeof(fa));
+    fa.ta = ta;
+    fa.bot.n_layers = m->n_bot - 1;
+    fa.top.n_layers = m->n_top - 1;
+    for (int32_t l = 0; l < m->n_bot; ++l) fa.bot.dim[l] = (int)m->ln_bot[l];
+    for (int32_t l = 0; l < m->n_top; ++l) fa.top.dim[l] = (int)m->ln_top[l];
+    size_t off = 0;
+    for (int32_t l = 0; l + 1 < m->n_bot; ++l) {
+        fa.bot.w[l] = packed ? packed + off : nullptr;
+        fa.bot.b[l] = m->bot_b[l];
+        off += packed_layer_floats(fa.bot.dim[l + 1], fa.bot.dim[l]);
+    }
+    for (int32_t l = 0; l + 2 < m->n_top; ++l) {
+        fa.top.w[l] = packed ? packed + off : nullptr;
+        fa.top.b[l] = m->top_b[l];
+        off += packed_layer_floats(fa.top.dim[l + 1], fa.top.dim[l]);
+    }
+    fa.last_w = m->top_w[m->n_top - 2];
+    fa.last_b = m->top_b[m->n_top - 2];
+    fa.dense = dense;
+    fa.out = out;
+    fa.B = batch;
+    fa.T = m->num_tables;
+    fa.D = m->emb_dim;
+    return fused_supported(fa, aligned);
+}
+
+// Floats of the packed weights of every layer but the last.
+size_t packed_floats(const dlrm_model_t* m) {
+    size_t n = 0;
+    for (int32_t l = 0; l + 1 < m->n_bot; ++l) n += packed_layer_floats((int)m->ln_bot[l + 1], (int)m->ln_bot[l]);
+    for (int32_t l = 0; l + 2 < m->n_top; ++l) n += packed_layer_floats((int)m->ln_top[l + 1], (int)m->ln_top[l]);
+    return n;
+}
+
+// Shape-only check of the single-launch path for a model (tables' alignment
+// included); used by the packing calls.
+bool model_fits_fused(const dlrm_model_t* m) {
+    if (validate_model(m, 1) != DLRM_OK || !m->emb_w) return false;
+    bool aligned = (m->emb_dim % 4 == 0);
+    for (int32_t t = 0; t < m->num_tables; ++t) aligned = aligned && m->emb_w[t] && al16(m->emb_w[t]);
     TableArgs ta;
-    bool aligned, multi_hot;
-    st = fill_tables(ta, T, batch, D, m->emb_w, m->rows, indices, n_indices, offsets, &aligned, &multi_hot);
-    if (st != DLRM_OK) return st;
+    memset(&ta, 0, sizeof(ta));
+    FusedArgs fa;
+    return fused_args(m, 1, nullptr, nullptr, ta, aligned, nullptr, fa);
+}
+
+// dlrm_forward takes the single-launch path up to this batch and while the
+// Linear weights stay well inside one XCD's 4 MiB L2 (every block streams all
+// of them).
+constexpr int64_t kFusedAutoMaxBatch = 16384;
+constexpr int64_t kFusedAutoMaxWeightBytes = 3 << 20;
+
+// Bytes of all Linear weights of the model.
+int64_t weight_bytes(const dlrm_model_t* m) {
+    int64_t n = 0;
+    for (int32_t l = 0; l + 1 < m->n_bot; ++l) n += m->ln_bot[l] * m->ln_bot[l + 1];
+    for (int32_t l = 0; l + 1 < m->n_top; ++l) n += m->ln_top[l] * m->ln_top[l + 1];
+    return 4 * n;
+}
+
+dlrm_status_t forward_layered(const dlrm_model_t* m, int64_t batch, const float* dense, float* out,
+                              const TableArgs& ta, bool aligned, bool multi_hot, void* workspace, size_t ws_bytes,
+                              hipStream_t s) {
+    const int32_t T = m->num_tables, D = m->emb_dim;
     Plan p;
     make_plan(m, batch, &p);
     if (!workspace || ((uintptr_t)workspace & 255u) != 0 || ws_bytes < p.total) return DLRM_E_WORKSPACE;
-
-    hipStream_t s = (hipStream_t)stream;
     char* ws = (char*)workspace;
     float* R = (float*)(ws + p.off_r);
     float* H[2] = {(float*)(ws + p.off_h0), (float*)(ws + p.off_h1)};
@@ -267,6 +337,81 @@ DLRM_API dlrm_status_t dlrm_forward(const dlrm_model_t* m, int64_t batch, const 
         ld_in = ld_o;
     }
     return DLRM_OK;
+}
+
+}  // namespace
+
+DLRM_API dlrm_status_t dlrm_forward_layered(const dlrm_model_t* m, int64_t batch, const float* dense,
+                                            const int64_t* const* indices, const int64_t* n_indices,
+                                            const int64_t* const* offsets, float* out, void* workspace,
+                                            size_t ws_bytes, void* stream) {
+    TableArgs ta;
+    bool aligned, multi_hot;
+    dlrm_status_t st = forward_args(m, batch, dense, indices, n_indices, offsets, out, ta, &aligned, &multi_hot);
+    if (st != DLRM_OK) return st;
+    return forward_layered(m, batch, dense, out, ta, aligned, multi_hot, workspace, ws_bytes, (hipStream_t)stream);
+}
+
+DLRM_API size_t dlrm_pack_weights_bytes(const dlrm_model_t* m) {
+    if (!m || !model_fits_fused(m)) return 0;
+    return packed_floats(m) * sizeof(float);
+}
+
+DLRM_API dlrm_status_t dlrm_pack_weights(const dlrm_model_t* m, float* packed, size_t bytes, void* stream) {
+    if (!m || !packed) return DLRM_E_NULL;
+    if (validate_model(m, 1) != DLRM_OK) return DLRM_E_SHAPE;
+    if (!m->bot_w || !m->top_w) return DLRM_E_NULL;
+    if (!model_fits_fused(m)) return DLRM_E_UNSUPPORTED;
+    if (((uintptr_t)packed & 255u) != 0 || bytes < packed_floats(m) * sizeof(float)) return DLRM_E_WORKSPACE;
+    for (int32_t l = 0; l + 1 < m->n_bot; ++l)
+        if (!m->bot_w[l]) return DLRM_E_NULL;
+    for (int32_t l = 0; l + 2 < m->n_top; ++l)
+        if (!m->top_w[l]) return DLRM_E_NULL;
+    hipStream_t s = (hipStream_t)stream;
+    size_t off = 0;
+    for (int32_t l = 0; l + 1 < m->n_bot; ++l) {
+        const int N = (int)m->ln_bot[l + 1], K = (int)m->ln_bot[l];
+        if (launch_pack_layer(m->bot_w[l], N, K, packed + off, s) != hipSuccess) return DLRM_E_HIP;
+        off += packed_layer_floats(N, K);
+    }
+    for (int32_t l = 0; l + 2 < m->n_top; ++l) {
+        const int N = (int)m->ln_top[l + 1], K = (int)m->ln_top[l];
+        if (launch_pack_layer(m->top_w[l], N, K, packed + off, s) != hipSuccess) return DLRM_E_HIP;
+        off += packed_layer_floats(N, K);
+    }
+    return DLRM_OK;
+}
+
+DLRM_API dlrm_status_t dlrm_forward_fused(const dlrm_model_t* m, int64_t batch, const float* dense,
+                                          const int64_t* const* indices, const int64_t* n_indices,
+                                          const int64_t* const* offsets, float* out, void* stream) {
+    TableArgs ta;
+    bool aligned, multi_hot;
+    dlrm_status_t st = forward_args(m, batch, dense, indices, n_indices, offsets, out, ta, &aligned, &multi_hot);
+    if (st != DLRM_OK) return st;
+    FusedArgs fa;
+    if (!fused_args(m, batch, dense, out, ta, aligned, m->packed_w, fa)) return DLRM_E_UNSUPPORTED;
+    if (!m->packed_w) return DLRM_E_NULL;
+    if (!al16(m->packed_w)) return DLRM_E_SHAPE;
+    return from_hip(launch_fused_forward(fa, aligned, multi_hot, (hipStream_t)stream));
+}
+
+DLRM_API dlrm_status_t dlrm_forward(const dlrm_model_t* m, int64_t batch, const float* dense,
+                                    const int64_t* const* indices, const int64_t* n_indices,
+                                    const int64_t* const* offsets, float* out, void* workspace, size_t ws_bytes,
+                                    void* stream) {
+    TableArgs ta;
+    bool aligned, multi_hot;
+    dlrm_status_t st = forward_args(m, batch, dense, indices, n_indices, offsets, out, ta, &aligned, &multi_hot);
+    if (st != DLRM_OK) return st;
+    Plan p;
+    make_plan(m, batch, &p);
+    if (!workspace || ((uintptr_t)workspace & 255u) != 0 || ws_bytes < p.total) return DLRM_E_WORKSPACE;
+    FusedArgs fa;
+    if (m->packed_w && al16(m->packed_w) && batch <= kFusedAutoMaxBatch &&
+        weight_bytes(m) <= kFusedAutoMaxWeightBytes && fused_args(m, batch, dense, out, ta, aligned, m->packed_w, fa))
+        return from_hip(launch_fused_forward(fa, aligned, multi_hot, (hipStream_t)stream));
+    return forward_layered(m, batch, dense, out, ta, aligned, multi_hot, workspace, ws_bytes, (hipStream_t)stream);
 }
 
 DLRM_API dlrm_status_t dlrm_embbag_check_indices(int32_t num_tables, int64_t batch, const int64_t* rows,

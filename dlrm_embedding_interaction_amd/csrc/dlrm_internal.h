@@ -15,6 +15,36 @@ constexpr size_t kInteractLdsBudget = 32 * 1024;     // target LDS per interacti
 constexpr size_t kMaxLdsBytes = 64 * 1024;           // hard LDS limit per block
 constexpr int kRowPad = 4;                           // floats of padding per LDS feature row
 
+// Single-launch forward limits: Linear layers per MLP, samples per block, LDS
+// per block (gfx950 gives a workgroup up to 160 KiB).
+constexpr int kFusedMaxLayers = 8;
+constexpr int kFusedSamples = 8;
+constexpr int kFusedThreads = 512;
+constexpr size_t kFusedMaxLds = 160 * 1024;
+
+// One MLP of the single-launch forward: layer l maps dim[l] -> dim[l + 1]
+// with packed weights w[l] (pack_layer_kernel layout) and bias b[l].
+struct MlpArgs {
+    const float* w[kFusedMaxLayers];
+    const float* b[kFusedMaxLayers];
+    int dim[kFusedMaxLayers + 1];
+    int n_layers;
+};
+
+// Kernel arguments of the single-launch forward (about 2.5 KiB).
+struct FusedArgs {
+    TableArgs ta;
+    MlpArgs bot, top;
+    const float* last_w;  // one-output last layer, nn.Linear layout (not packed)
+    const float* last_b;
+    const float* dense;
+    float* out;
+    int64_t B;
+    int T, D;
+    int lda;     // row stride of the LDS activation buffers (set by the launcher)
+    int dsplit;  // d split of the interaction dots (set by the launcher)
+};
+
 // Arguments of the device-side bag-data check.
 struct CheckArgs {
     const int64_t* idx[DLRM_MAX_TABLES];
@@ -53,6 +83,15 @@ hipError_t launch_interact(const TableArgs* ta, const float* emb, int T, int D, 
 // General bags (mode, weights, include_last_offset, padding) into out (B, T, D).
 hipError_t launch_embbag_ex(const BagArgs& ba, int T, int D, int64_t B, int mode, int last_off, bool idx32,
                             bool aligned16, bool multi_hot, float* out, hipStream_t s);
+
+// Whole forward in one launch (kFusedSamples samples per block).  Returns
+// hipErrorInvalidValue when the model is outside fused_supported.
+bool fused_supported(const FusedArgs& fa, bool aligned16);
+size_t fused_lds_bytes(const FusedArgs& fa, int samples);
+hipError_t launch_fused_forward(FusedArgs fa, bool aligned16, bool multi_hot, hipStream_t s);
+// Floats of one packed (N, K) layer, rounded up to 256 bytes, and its packing.
+size_t packed_layer_floats(int N, int K);
+hipError_t launch_pack_layer(const float* W, int N, int K, float* packed, hipStream_t s);
 
 hipError_t launch_check_indices(const CheckArgs& ca, int T, int64_t B, int32_t* bad, hipStream_t s);
 

@@ -34,68 +34,9 @@
 #include "dlrm_device.h"
 #include "dlrm_internal.h"
 #include "rowvec.h"
+#include "bag_dots.h"
 
 namespace dlrm {
-
-// Sum U bags per lane group.  Bag q[u] (-1 = none) is local bag number
-// q = sl * T + t of sample b_base + sl.  Lane lg of the group owns elements
-// (c * G + lg) * VEC .. + VEC-1 of the row for c < C.  Rows of one bag are
-// added in increasing k, R of them fetched per step.
-template <int VEC, int G, int C, int U, int R>
-__device__ __forceinline__ void gather_bags(const TableArgs& ta, int T, int D, int64_t B, int64_t b_base,
-                                            const int (&q)[U], int lg,
-                                            typename Vec<VEC>::T (&acc)[U][C]) {
-    using V = Vec<VEC>;
-    const float* wp[U];
-    const int64_t* ip[U];
-    int len[U];
-    int maxlen = 0;
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        len[u] = 0;
-        wp[u] = nullptr;
-        ip[u] = nullptr;
-        if (q[u] >= 0) {
-            const int sl = q[u] / T;
-            const int t = q[u] - sl * T;
-            const int64_t b = b_base + sl;
-            const int64_t* off = ta.off[t];
-            const int64_t s = off[b];
-            const int64_t e = (b + 1 < B) ? off[b + 1] : ta.nidx[t];
-            len[u] = (int)(e - s);
-            wp[u] = ta.w[t];
-            ip[u] = ta.idx[t] + s;
-        }
-        maxlen = max(maxlen, len[u]);
-#pragma unroll
-        for (int c = 0; c < C; ++c) acc[u][c] = V::zero();
-    }
-    for (int r0 = 0; r0 < maxlen; r0 += R) {
-        int64_t row[R][U];
-#pragma unroll
-        for (int rr = 0; rr < R; ++rr)
-#pragma unroll
-            for (int u = 0; u < U; ++u) row[rr][u] = (r0 + rr < len[u]) ? ip[u][r0 + rr] : -1;
-        typename V::T v[R][U][C];
-#pragma unroll
-        for (int rr = 0; rr < R; ++rr)
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-#pragma unroll
-                for (int c = 0; c < C; ++c) {
-                    const int e = (c * G + lg) * VEC;
-                    v[rr][u][c] = (row[rr][u] >= 0 && e < D) ? V::load(wp[u] + row[rr][u] * D + e) : V::zero();
-                }
-#pragma unroll
-        for (int rr = 0; rr < R; ++rr)
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-                if (row[rr][u] >= 0) {
-#pragma unroll
-                    for (int c = 0; c < C; ++c) acc[u][c] = V::add(acc[u][c], v[rr][u][c]);
-                }
-    }
-}
 
 // ---- standalone multi-table bags: out (B, T, D) -------------------------------
 template <int VEC, int G, int C, int U, int R>
@@ -197,93 +138,11 @@ __global__ __launch_bounds__(kBlock) void interact_kernel(TableArgs ta, const fl
     __syncthreads();
 
     // 3. dots
-    const int npairs = nb * P;
-    if constexpr (RT == 0) {
-        // one flat pair index per lane group at a time
-        for (int w = g; w < npairs; w += NG) {
-            const int s = w / P;
-            const int p = w - s * P;
-            int i, j;
-            pair_from_flat(p, i, j);
-            const float* si = S + ((size_t)s * F + i) * LDR;
-            const float* sj = S + ((size_t)s * F + j) * LDR;
-            float part = 0.f;
-#pragma unroll
-            for (int c = 0; c < C; ++c) {
-                const int e = (c * G + lg) * VEC;
-                if (e < D) part = V::dot(V::load(si + e), V::load(sj + e), part);
-            }
-            const float tot = group_sum<G>(part);
-            if (lg == 0) Zs[w] = tot;
-        }
-    } else {
-        // RT x RT blocks: rows i = 1 + RT*I + a, columns j = RT*J + b, J <= I;
-        // block number q = I(I+1)/2 + J, decoded as the pair (I+1, J).  With
-        // dsplit > 1, dsplit neighbouring lanes take equal slices of d for the
-        // same block and add their partial blocks with DPP (xor 1, xor 2).
-        const int NI = (F - 1 + RT - 1) / RT;
-        const int nblk = NI * (NI + 1) / 2;
-        const int dlen = D / dsplit;
-        for (int w = tid; w < nb * nblk * dsplit; w += kBlock) {
-            const int wq = w / dsplit;
-            const int h = w - wq * dsplit;
-            const int s = wq / nblk;
-            const int q = wq - s * nblk;
-            int I1, J;
-            pair_from_flat(q, I1, J);
-            const int i0 = 1 + RT * (I1 - 1);
-            const int j0 = RT * J;
-            const float* Sb = S + (size_t)s * F * LDR + h * dlen;
-            const float* ri[RT];
-            const float* rj[RT];
-#pragma unroll
-            for (int a = 0; a < RT; ++a) {
-                ri[a] = Sb + min(i0 + a, F - 1) * LDR;   // rows past the end are read but never stored
-                rj[a] = Sb + min(j0 + a, F - 1) * LDR;
-            }
-            float acc[RT][RT];
-#pragma unroll
-            for (int a = 0; a < RT; ++a)
-#pragma unroll
-                for (int b = 0; b < RT; ++b) acc[a][b] = 0.f;
-            for (int d = 0; d < dlen; d += VEC) {
-                typename V::T u[RT], v[RT];
-#pragma unroll
-                for (int a = 0; a < RT; ++a) {
-                    u[a] = V::load(ri[a] + d);
-                    v[a] = V::load(rj[a] + d);
-                }
-#pragma unroll
-                for (int a = 0; a < RT; ++a)
-#pragma unroll
-                    for (int b = 0; b < RT; ++b) acc[a][b] = V::dot(u[a], v[b], acc[a][b]);
-            }
-            if (dsplit > 1) {
-#pragma unroll
-                for (int a = 0; a < RT; ++a)
-#pragma unroll
-                    for (int b = 0; b < RT; ++b) {
-                        acc[a][b] += dpp_quad_xor1(acc[a][b]);
-                        if (dsplit > 2) acc[a][b] += dpp_quad_xor2(acc[a][b]);
-                    }
-            }
-            if (h == 0) {
-#pragma unroll
-                for (int a = 0; a < RT; ++a) {
-                    const int i = i0 + a;
-#pragma unroll
-                    for (int b = 0; b < RT; ++b) {
-                        const int j = j0 + b;
-                        if (i < F && j < i) Zs[s * P + i * (i - 1) / 2 + j] = acc[a][b];
-                    }
-                }
-            }
-        }
-    }
+    pair_dots<VEC, G, C, RT>(S, F, D, LDR, nb, Zs, P, dsplit);
     __syncthreads();
 
     // 4. write Z (and x) rows
-    for (int e = tid; e < npairs; e += kBlock) {
+    for (int e = tid; e < nb * P; e += kBlock) {
         const int s = e / P;
         const int p = e - s * P;
         out[(b0 + s) * ld_out + col_z + p] = Zs[e];

@@ -1,0 +1,421 @@
+// fused_forward.hip -- the whole DLRMv1 forward in one launch on gfx950.
+//
+// The pages' fastest path runs one kernel per forward ("dlrm --mega" on
+// "luminal compare dlrm-fused-kernels...dlrm-pt2-megakernel": module doc of
+// dlrm_megakernel.rs and cuda_source steps 1-7): bottom MLP with ReLU after
+// every layer, bags, stacked features with x first, strict-lower-triangle
+// dots, R = [x | Z], top MLP with ReLU on hidden layers and a sigmoid on the
+// one-output last layer.  There one thread carries one sample through the
+// whole network in registers; with 512-wide layers that cannot fit, so here a
+// block of eight waves carries S samples:
+//
+//  * activations live in LDS, two (S, lda) ping-pong buffers, the S feature
+//    stacks in a third region (S, F, D + 4);
+//  * every Linear layer streams its weight rows straight from L2 into
+//    registers (each weight is read once per block and used for all S
+//    samples) and multiplies them on the matrix cores with
+//    v_mfma_f32_4x4x1f32: one instruction is 16 blocks of 4x4x1, and lane
+//    l = 16 fg + 4 kg + e supplies W[f = 4 fg + e][k = 4 kg + q] as A and
+//    act[sample e][k] as B, so one instruction covers 16 features x 4 samples
+//    x 4 k values at the full fp32 MFMA rate even with 4-sample groups; the
+//    4 k groups are added afterwards with two DPP row shifts;
+//  * the bags are gathered with the same lane-group code as the standalone
+//    bag kernel and the dots reuse the interaction kernel's LDS routine;
+//  * nothing leaves the block but the S sigmoid outputs.
+//
+// Samples are independent, so blocks never communicate; the weights of one
+// forward (a few MB) stay resident in every XCD's L2.
+#include "dlrm_device.h"
+#include "dlrm_internal.h"
+#include "rowvec.h"
+#include "bag_dots.h"
+
+namespace dlrm {
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+// Explicit LDS accesses: the activation buffers are reached through pointer
+// arithmetic on the dynamic LDS array, and the casts make sure the compiler
+// emits ds_read / ds_write (a flat access would be counted with the global
+// weight loads and make every wait cover the whole prefetch ring).
+typedef __attribute__((address_space(3))) float lds_float;
+typedef __attribute__((address_space(3))) floatx4 lds_floatx4;
+__device__ __forceinline__ floatx4 lds_load4(const float* p) { return *(const lds_floatx4*)(const lds_float*)p; }
+__device__ __forceinline__ float lds_load(const float* p) { return *(const lds_float*)p; }
+__device__ __forceinline__ void lds_store4(float* p, floatx4 v) { *(lds_floatx4*)(lds_float*)p = v; }
+__device__ __forceinline__ void lds_store(float* p, float v) { *(lds_float*)p = v; }
+
+__device__ __forceinline__ float dpp_row_shr4(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x114, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float dpp_row_shr8(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x118, 0xF, 0xF, false));
+}
+
+// out[s][c] = 0 for s < S and c in [c0, c1) (all threads of the block).
+template <int S>
+__device__ __forceinline__ void zero_columns(float* out, int ldo, int c0, int c1) {
+    const int w = c1 - c0;
+    for (int i = threadIdx.x; i < S * w; i += kFusedThreads) {
+        const int s = i / w;
+        lds_store(out + s * ldo + c0 + (i - s * w), 0.f);
+    }
+}
+
+// Packed weights of one layer (N, K): tiles of 16 output features x 16 inputs,
+// tile (t, kc) at float offset (t * ceil(K / 16) + kc) * 256, holding for lane
+// l = 16 fg + 4 kg + e the four weights W[16 t + 4 fg + e][16 kc + 4 kg + q],
+// q = 0..3, and zeros past N or K.
+__global__ __launch_bounds__(kBlock) void pack_layer_kernel(const float* __restrict__ W, int N, int K,
+                                                            float* __restrict__ packed) {
+    const int nkc = (K + 15) >> 4;
+    const int64_t total = (int64_t)((N + 15) >> 4) * nkc * 64;
+    const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    if (i >= total) return;
+    const int lane = (int)(i & 63);
+    const int64_t tk = i >> 6;
+    const int t = (int)(tk / nkc);
+    const int kc = (int)(tk - (int64_t)t * nkc);
+    const int n = 16 * t + 4 * (lane >> 4) + (lane & 3);
+    const int k0 = 16 * kc + 4 * ((lane >> 2) & 3);
+    floatx4 v;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] = (n < N && k0 + q < K) ? W[(int64_t)n * K + k0 + q] : 0.f;
+    *reinterpret_cast<floatx4*>(packed + i * 4) = v;
+}
+
+// out[s][n] = act(sum_k in[s][k] W[n][k] + bias[n]) for s < S, n < N, with in
+// and out in LDS (row strides ldi, ldo) and W packed as above.  The N outputs
+// form tiles of 16 features; wave w takes tiles w, w + NW, ... in passes of TW
+// tiles.  One step covers KU chunks of 16 k values; the weights of a step are
+// requested PD steps ahead into a register ring whose slots are fixed at
+// compile time (no register copies, so the wait before a step's MFMAs covers
+// only that step's loads).  Each load of a wave is 1 KiB of contiguous packed
+// weights.  in[s][k] must be zero for k in [K, round_up(K, 64)); on return
+// out[s][n] is zero for n in [N, round_up(N, 64)).
+template <int S, int TW, int KU, int PD>
+__device__ __forceinline__ void mlp_layer(const float* in, int ldi, int K, const float* __restrict__ Wp,
+                                          const float* __restrict__ bias, int N, bool relu, float* out, int ldo) {
+    constexpr int SG = S / 4;
+    constexpr int NW = kFusedThreads / 64;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int e = lane & 3;
+    const int kg = (lane >> 2) & 3;
+    const int fg = lane >> 4;
+    const int ntile = (N + 15) >> 4;
+    const int nkc = (K + 15) >> 4;
+    const int nkb = (K + 16 * KU - 1) / (16 * KU);
+    const float* arow[SG];
+#pragma unroll
+    for (int sg = 0; sg < SG; ++sg) arow[sg] = in + (4 * sg + e) * ldi + 4 * kg;
+
+    for (int t0 = 0; t0 < ntile; t0 += NW * TW) {
+        const float* wtile[TW];
+        floatx4 acc[TW][SG];
+        floatx4 bv[TW];
+#pragma unroll
+        for (int u = 0; u < TW; ++u) {
+            // tiles past the last are read (clamped) but never stored
+            const int t = min(t0 + wave + NW * u, ntile - 1);
+            wtile[u] = Wp + ((int64_t)t * nkc * 64 + lane) * 4;
+            const int n0 = 16 * t + 4 * fg;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) bv[u][r] = bias[min(n0 + r, N - 1)];  // requested before the weights
+#pragma unroll
+            for (int sg = 0; sg < SG; ++sg) acc[u][sg] = floatx4{0.f, 0.f, 0.f, 0.f};
+        }
+        floatx4 ring[PD][TW][KU];
+        // chunks past the last are read (clamped) and meet zero activations
+        auto loadw = [&](int kb, floatx4 (&w)[TW][KU]) {
+#pragma unroll
+            for (int u = 0; u < TW; ++u)
+#pragma unroll
+                for (int c = 0; c < KU; ++c)
+                    w[u][c] = *reinterpret_cast<const floatx4*>(wtile[u] + min(kb * KU + c, nkc - 1) * 256);
+        };
+        auto step = [&](int kb, const floatx4 (&w)[TW][KU]) {
+            floatx4 a[KU][SG];
+#pragma unroll
+            for (int c = 0; c < KU; ++c)
+#pragma unroll
+                for (int sg = 0; sg < SG; ++sg) a[c][sg] = lds_load4(arow[sg] + (kb * KU + c) * 16);
+#pragma unroll
+            for (int c = 0; c < KU; ++c)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+#pragma unroll
+                    for (int u = 0; u < TW; ++u)
+#pragma unroll
+                        for (int sg = 0; sg < SG; ++sg)
+                            acc[u][sg] =
+                                __builtin_amdgcn_mfma_f32_4x4x1f32(w[u][c][q], a[c][sg][q], acc[u][sg], 0, 0, 0);
+        };
+#pragma unroll
+        for (int p = 0; p < PD; ++p) loadw(min(p, nkb - 1), ring[p]);
+        // whole trips of PD steps (a loop with a single exit, so the waits
+        // before each step count only that step's loads), then the rest
+        const int trips = nkb / PD;
+        for (int tr = 0; tr < trips; ++tr) {
+#pragma unroll
+            for (int p = 0; p < PD; ++p) {
+                const int kb = tr * PD + p;
+                step(kb, ring[p]);
+                loadw(min(kb + PD, nkb - 1), ring[p]);
+            }
+        }
+        const int rest = nkb - trips * PD;
+#pragma unroll
+        for (int p = 0; p < PD; ++p)
+            if (p < rest) step(trips * PD + p, ring[p]);
+        // VGPR r of lane 16 fg + 4 kg + e holds the partial sum over the k
+        // group kg for feature 16 t + 4 fg + r and sample 4 sg + e; two row
+        // shifts leave the total over kg in the lanes with kg = 3.
+#pragma unroll
+        for (int u = 0; u < TW; ++u) {
+            const int t = t0 + wave + NW * u;
+            if (t >= ntile) break;
+            const int n0 = 16 * t + 4 * fg;
+#pragma unroll
+            for (int sg = 0; sg < SG; ++sg) {
+                floatx4 v = acc[u][sg];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    v[r] += dpp_row_shr4(v[r]);
+                    v[r] += dpp_row_shr8(v[r]);
+                }
+                if (kg == 3) {
+                    floatx4 o;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float y = v[r] + bv[u][r];
+                        o[r] = (n0 + r < N) ? (relu ? fmaxf(y, 0.f) : y) : 0.f;
+                    }
+                    lds_store4(out + (4 * sg + e) * ldo + n0, o);
+                }
+            }
+        }
+    }
+    zero_columns<S>(out, ldo, (N + 15) & ~15, (N + 63) & ~63);
+}
+
+// Layer dispatch: TW = tiles per wave and pass, KU chunks of 16 k per step and
+// PD steps in flight, so that each of the 8 waves keeps 24 weight loads (24
+// KiB) outstanding -- the L2 stream into one CU is latency-bound, so the
+// more requests in flight the higher its rate.
+template <int S>
+__device__ __forceinline__ void mlp_layer_any(const float* in, int ldi, int K, const float* Wp, const float* bias,
+                                              int N, bool relu, float* out, int ldo) {
+    constexpr int NW = kFusedThreads / 64;
+    const int ntile = (N + 15) >> 4;
+    const int tw = (ntile + NW - 1) / NW;
+#define DLRM_LAYER(TW_, KU_, PD_)                                               \
+    {                                                                           \
+        mlp_layer<S, TW_, KU_, PD_>(in, ldi, K, Wp, bias, N, relu, out, ldo);   \
+        return;                                                                 \
+    }
+    if (tw <= 1) DLRM_LAYER(1, 4, 6)
+    if (tw <= 2) DLRM_LAYER(2, 2, 6)
+    DLRM_LAYER(4, 1, 6)
+#undef DLRM_LAYER
+}
+
+// y[s] = sigmoid(<in[s], w> + b) for the one-output last layer, with w staged
+// in LDS: wave w takes samples w, w + NW, ...
+template <int S>
+__device__ __forceinline__ void last_layer(const float* in, int ldi, int K, const float* w, float b,
+                                           float* __restrict__ y, int nb) {
+    constexpr int NW = kFusedThreads / 64;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    for (int s = wave; s < nb; s += NW) {
+        float acc = 0.f;
+        for (int k = lane; k < K; k += 64) acc = fmaf(lds_load(in + s * ldi + k), lds_load(w + k), acc);
+        acc = group_sum<64>(acc);
+        if (lane == 0) y[s] = 1.f / (1.f + expf(-(acc + b)));
+    }
+}
+
+template <int S, int G, int U, int R, int RT>
+__global__ __launch_bounds__(kFusedThreads) void fused_forward_kernel(FusedArgs fa) {
+    using V = Vec<4>;
+    constexpr int NT = kFusedThreads;
+    constexpr int NG = NT / G;
+    extern __shared__ float4 lds4[];
+    const int lda = fa.lda;
+    const int T = fa.T, D = fa.D;
+    const int F = T + 1;
+    const int LDR = D + kRowPad;
+    // buffers by offset from the LDS array (no pointer array: its address
+    // space would be lost)
+    float* const lds = reinterpret_cast<float*>(lds4);
+    auto buf = [&](int i) { return lds + i * S * lda; };
+    float* feat = lds + 2 * S * lda;
+    float* wlast = feat + S * F * LDR;
+    const int klast = fa.top.dim[fa.top.n_layers - 1];
+    const int tid = threadIdx.x;
+    const int64_t b0 = (int64_t)blockIdx.x * S;
+    const int nb = (int)min((int64_t)S, fa.B - b0);
+    const float blast = fa.last_b[0];
+
+    // 0. zero both activation buffers (reads past a layer's K must be finite)
+    for (int i = tid; i < (2 * S * lda) / 4; i += NT) lds4[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    __syncthreads();
+
+    // 1. dense rows into buffer 0, the last layer's weights into LDS
+    const int n0 = fa.bot.dim[0];
+    for (int i = tid; i < nb * n0; i += NT) {
+        const int s = i / n0;
+        const int k = i - s * n0;
+        lds_store(buf(0) + s * lda + k, fa.dense[(b0 + s) * n0 + k]);
+    }
+    for (int k = tid; k < klast; k += NT) lds_store(wlast + k, fa.last_w[k]);
+
+    // 2. bags of this block's samples into feature rows 1..T
+    {
+        const int lg = tid % G;
+        const int g = tid / G;
+        const int nbag = nb * T;
+        for (int qb = 0; qb < nbag; qb += NG * U) {
+            int q[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int qq = qb + u * NG + g;
+                q[u] = qq < nbag ? qq : -1;
+            }
+            typename V::T acc[U][1];
+            gather_bags<4, G, 1, U, R>(fa.ta, T, D, fa.B, b0, q, lg, acc);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (q[u] < 0) continue;
+                const int s = q[u] / T;
+                const int t = q[u] - s * T;
+                if (lg * 4 < D) V::store(feat + ((size_t)s * F + 1 + t) * LDR + lg * 4, acc[u][0]);
+            }
+        }
+    }
+    __syncthreads();
+
+    // 3. bottom MLP, ReLU after every layer
+    int cur = 0;
+    for (int l = 0; l < fa.bot.n_layers; ++l) {
+        mlp_layer_any<S>(buf(cur), lda, fa.bot.dim[l], fa.bot.w[l], fa.bot.b[l], fa.bot.dim[l + 1], true,
+                         buf(cur ^ 1), lda);
+        __syncthreads();
+        cur ^= 1;
+    }
+
+    // 4. x into feature row 0 and into R = [x | Z] (the other buffer)
+    float* Rb = buf(cur ^ 1);
+    for (int i = tid; i < nb * D; i += NT) {
+        const int s = i / D;
+        const int d = i - s * D;
+        const float v = lds_load(buf(cur) + s * lda + d);
+        lds_store(feat + (size_t)s * F * LDR + d, v);
+        lds_store(Rb + s * lda + d, v);
+    }
+    __syncthreads();
+
+    // 5. strict-lower-triangle dots into R[:, D:D+P]
+    pair_dots<4, G, 1, RT, NT>(feat, F, D, LDR, nb, Rb + D, lda, fa.dsplit);
+    zero_columns<S>(Rb, lda, D + F * (F - 1) / 2, (D + F * (F - 1) / 2 + 63) & ~63);
+    __syncthreads();
+    cur ^= 1;
+
+    // 6. top hidden layers with ReLU, 7. last layer with sigmoid
+    const int nt = fa.top.n_layers;
+    for (int l = 0; l + 1 < nt; ++l) {
+        mlp_layer_any<S>(buf(cur), lda, fa.top.dim[l], fa.top.w[l], fa.top.b[l], fa.top.dim[l + 1], true,
+                         buf(cur ^ 1), lda);
+        __syncthreads();
+        cur ^= 1;
+    }
+    last_layer<S>(buf(cur), lda, klast, wlast, blast, fa.out + b0, nb);
+}
+
+// ---- host side ------------------------------------------------------------------
+
+static inline int round_up_int(int v, int a) { return (v + a - 1) / a * a; }
+
+// Row stride of the activation buffers: every width the layers read, rounded
+// up to the 64 k values one weight step can cover, plus 8 floats so that the
+// 4 sample rows of one read start 8 banks apart.
+int fused_lda(const FusedArgs& fa) {
+    int w = fa.bot.dim[0];
+    for (int l = 0; l <= fa.bot.n_layers; ++l) w = w > fa.bot.dim[l] ? w : fa.bot.dim[l];
+    for (int l = 0; l <= fa.top.n_layers; ++l) w = w > fa.top.dim[l] ? w : fa.top.dim[l];
+    return round_up_int(w, 64) + 8;
+}
+
+size_t fused_lds_bytes(const FusedArgs& fa, int S) {
+    const int F = fa.T + 1;
+    const int klast = fa.top.dim[fa.top.n_layers - 1];
+    return sizeof(float) * ((size_t)2 * S * fused_lda(fa) + (size_t)S * F * (fa.D + kRowPad) + klast);
+}
+
+template <int S, int G, int U, int R, int RT>
+static hipError_t launch_fused_t(const FusedArgs& fa, hipStream_t s) {
+    const size_t lds = fused_lds_bytes(fa, S);
+    static bool attr_set = false;  // one attribute call per instantiation and process
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void*)fused_forward_kernel<S, G, U, R, RT>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)kFusedMaxLds);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    const int64_t blocks = (fa.B + S - 1) / S;
+    hipLaunchKernelGGL((fused_forward_kernel<S, G, U, R, RT>), dim3((unsigned)blocks), dim3(kFusedThreads), lds, s,
+                       fa);
+    return hipGetLastError();
+}
+
+size_t packed_layer_floats(int N, int K) {
+    const size_t f = (size_t)((N + 15) / 16) * ((K + 15) / 16) * 256;
+    return (f + 63) / 64 * 64;  // each layer starts 256-byte aligned
+}
+
+hipError_t launch_pack_layer(const float* W, int N, int K, float* packed, hipStream_t s) {
+    const int64_t total = (int64_t)((N + 15) / 16) * ((K + 15) / 16) * 64;
+    hipLaunchKernelGGL(pack_layer_kernel, dim3((unsigned)((total + kBlock - 1) / kBlock)), dim3(kBlock), 0, s, W, N,
+                       K, packed);
+    return hipGetLastError();
+}
+
+bool fused_supported(const FusedArgs& fa, bool aligned16) {
+    if (!aligned16 || fa.D % 4 != 0 || fa.D < 16 || fa.D > 256) return false;
+    if (fa.bot.n_layers < 1 || fa.top.n_layers < 1) return false;
+    if (fa.bot.n_layers > kFusedMaxLayers || fa.top.n_layers > kFusedMaxLayers) return false;
+    return fused_lds_bytes(fa, kFusedSamples) <= kFusedMaxLds;
+}
+
+hipError_t launch_fused_forward(FusedArgs fa, bool aligned16, bool multi_hot, hipStream_t s) {
+    if (!fused_supported(fa, aligned16)) return hipErrorInvalidValue;
+    fa.lda = fused_lda(fa);
+    const int F = fa.T + 1;
+    const int n4 = (F - 1 + 3) / 4;
+    const int items = kFusedSamples * n4 * (n4 + 1) / 2;
+    int dsplit = 1;
+    while (dsplit < 4 && items * dsplit * 2 <= kFusedThreads && fa.D % (4 * dsplit * 2) == 0) dsplit *= 2;
+    fa.dsplit = dsplit;
+    const int g = pow2_at_least((fa.D + 3) / 4);
+    constexpr int S = kFusedSamples;
+#define FUSED_G(G_)                                                                                 \
+    case G_:                                                                                        \
+        if (F <= 12) {                                                                              \
+            if (multi_hot) return launch_fused_t<S, G_, 4, 4, 0>(fa, s);                            \
+            return launch_fused_t<S, G_, 8, 1, 0>(fa, s);                                           \
+        }                                                                                           \
+        if (multi_hot) return launch_fused_t<S, G_, 4, 4, 4>(fa, s);                                \
+        return launch_fused_t<S, G_, 8, 1, 4>(fa, s);
+    switch (g) {
+        FUSED_G(4)
+        FUSED_G(8)
+        FUSED_G(16)
+        FUSED_G(32)
+        FUSED_G(64)
+        default: return hipErrorInvalidValue;
+    }
+#undef FUSED_G
+}
+
+}  // namespace dlrm

@@ -78,6 +78,10 @@ typedef enum dlrm_status {
  *   bot_w[l]           (ln_bot[l+1], ln_bot[l]) nn.Linear layout, bot_b[l] (ln_bot[l+1])
  *   top_w[l]           (ln_top[l+1], ln_top[l]),                top_b[l] (ln_top[l+1])
  *   emb_w[t]           (rows[t], emb_dim)
+ *   packed_w           NULL, or device memory holding the hidden-layer weights
+ *                      in the order the single-launch forward reads them,
+ *                      written by dlrm_pack_weights from the bot_w / top_w
+ *                      above (pack again after changing them)
  * Biases may not be NULL.
  */
 typedef struct dlrm_model {
@@ -93,6 +97,7 @@ typedef struct dlrm_model {
     const float* const* bot_b;
     const float* const* top_w;
     const float* const* top_b;
+    const float* packed_w;
 } dlrm_model_t;
 
 /*
@@ -263,13 +268,63 @@ size_t dlrm_forward_workspace_bytes(const dlrm_model_t* m, int64_t batch);
  *   offsets    host[T] of device pointers (B) int64, as dlrm_embbag_sum
  *   out        device (B) fp32 probabilities
  *   workspace  device, >= dlrm_forward_workspace_bytes(m, B), 256-byte aligned
- * Enqueues a few kernels on `stream`; the workspace must not be used by
- * another call until they finish.
+ * Enqueues either one kernel (the single-launch path of dlrm_forward_fused,
+ * taken when m->packed_w is set, the model fits that path and its weights are
+ * small enough to stay in L2) or a few kernels (dlrm_forward_layered) on
+ * `stream`; the workspace must
+ * not be used by another call until they finish.  Both paths compute the same
+ * function; results agree to rounding.
  */
 dlrm_status_t dlrm_forward(const dlrm_model_t* m, int64_t batch, const float* dense,
                            const int64_t* const* indices, const int64_t* n_indices,
                            const int64_t* const* offsets, float* out, void* workspace,
                            size_t ws_bytes, void* stream);
+
+/*
+ * dlrm_forward_layered -- dlrm_forward as a sequence of kernels: one MFMA
+ * GEMM per Linear layer (bias and activation in its epilogue), one fused bag
+ * + interaction kernel writing R = [x | Z] into the workspace, and a dot
+ * product kernel with the sigmoid for the last layer.  Same arguments and
+ * errors as dlrm_forward.
+ */
+dlrm_status_t dlrm_forward_layered(const dlrm_model_t* m, int64_t batch, const float* dense,
+                                   const int64_t* const* indices, const int64_t* n_indices,
+                                   const int64_t* const* offsets, float* out, void* workspace,
+                                   size_t ws_bytes, void* stream);
+
+/*
+ * dlrm_pack_weights_bytes -- bytes of the packed weights of model m for the
+ * single-launch forward, or 0 when m is invalid or outside that path's limits
+ * (see dlrm_forward_fused).  Host only.
+ *
+ * dlrm_pack_weights -- write them.  Every Linear layer but the one-output
+ * last layer is stored as tiles of 16 output features x 16 inputs, each tile
+ * as 64 lanes x 4 floats in the operand order of the kernel's matrix-core
+ * instruction, zero past the layer's edges, so that one wave reads 1 KiB of
+ * contiguous memory per load.  packed: device, >= dlrm_pack_weights_bytes(m)
+ * bytes, 256-byte aligned; written asynchronously on `stream`.  The caller
+ * stores the pointer in m->packed_w and packs again after changing weights.
+ */
+size_t dlrm_pack_weights_bytes(const dlrm_model_t* m);
+dlrm_status_t dlrm_pack_weights(const dlrm_model_t* m, float* packed, size_t bytes, void* stream);
+
+/*
+ * dlrm_forward_fused -- dlrm_forward in a single kernel launch, the pages'
+ * "one kernel per forward" design (dlrm_megakernel.rs module doc and
+ * cuda_source steps 1-7 on "luminal compare dlrm-fused-kernels...
+ * dlrm-pt2-megakernel").  Each block carries 8 samples through the whole
+ * network with its activations in LDS and the packed weights (m->packed_w,
+ * DLRM_E_NULL when absent) read from L2; no workspace is used.  Arguments as
+ * dlrm_forward without the workspace.
+ * Returns DLRM_E_UNSUPPORTED, and enqueues nothing, unless emb_dim % 4 == 0,
+ * 16 <= emb_dim <= 256, every table is 16-byte aligned, each MLP has at most 8
+ * Linear layers and the block's LDS (2 x 8 x (widest layer rounded up to 64,
+ * plus 8) + 8 x (T + 1) x (emb_dim + 4) + ln_top[n_top-2] floats) fits in
+ * 160 KiB.
+ */
+dlrm_status_t dlrm_forward_fused(const dlrm_model_t* m, int64_t batch, const float* dense,
+                                 const int64_t* const* indices, const int64_t* n_indices,
+                                 const int64_t* const* offsets, float* out, void* stream);
 
 /*
  * dlrm_embbag_check_indices -- validate the bag data of dlrm_embbag_sum on the
@@ -298,7 +353,7 @@ const char* dlrm_status_string(dlrm_status_t status);
 
 /* ABI version of this header, bumped on any incompatible change. */
 int32_t dlrm_abi_version(void);
-#define DLRM_ABI_VERSION 1
+#define DLRM_ABI_VERSION 2
 
 #ifdef __cplusplus
 }

@@ -264,9 +264,9 @@ def test_linear_integer_exact():
 # --- whole forward ------------------------------------------------------------------
 
 
-def _forward_check(inp_cpu, g, orc, rows=None, tol=E2E_TOL):
+def _forward_check(inp_cpu, g, orc, rows=None, tol=E2E_TOL, path="auto"):
     model = dl.Model.from_inputs(g)
-    out = model.forward(g.dense, g.indices, g.offsets)
+    out = model.forward(g.dense, g.indices, g.offsets, path=path)
     torch.cuda.synchronize()
     got = out.cpu().double().numpy()
     if rows is None:
@@ -280,11 +280,12 @@ def _forward_check(inp_cpu, g, orc, rows=None, tol=E2E_TOL):
     return model, out, err.max()
 
 
+@pytest.mark.parametrize("path", ["auto", "fused", "layered"])
 @pytest.mark.parametrize("name", ["tiny", "page4", "manytable"])
-def test_forward_e2e(name, orc):
-    log(f"forward {name}")
+def test_forward_e2e(name, path, orc):
+    log(f"forward {name} ({path})")
     inp = di.make_inputs(di.get(name))
-    _, _, e = _forward_check(inp, on_gpu(inp), orc)
+    _, _, e = _forward_check(inp, on_gpu(inp), orc, path=path)
     log(f"  max |err| = {e:.3g}")
 
 
@@ -317,14 +318,15 @@ def test_forward_layerwise_through_standalone_calls(orc):
     assert torch.allclose(out, h[:, 0], atol=1e-6, rtol=0)
 
 
+@pytest.mark.parametrize("path", ["fused", "layered"])
 @pytest.mark.parametrize("B,T", [(16, 1), (16, 32), (64, 8), (256, 4), (2048, 16), (4096, 1), (16384, 8),
                                  (16384, 32)])
-def test_forward_sweep_cells(B, T, orc):
-    log(f"sweep cell b={B} t={T}")
+def test_forward_sweep_cells(B, T, path, orc):
+    log(f"sweep cell b={B} t={T} ({path})")
     w = di.sweep(B, T)
     g = di.make_inputs(w, device=dev())
     rows = sample_rows(B, 512, B + T)
-    _forward_check(None, g, orc, rows=rows)
+    _forward_check(None, g, orc, rows=rows, path=path)
 
 
 def test_forward_stress_sampled(orc):
@@ -338,14 +340,16 @@ def test_forward_stress_sampled(orc):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("path", ["fused", "layered"])
 @pytest.mark.parametrize("B", [1, 2, 3, 5, 17, 100])
-def test_forward_small_and_ragged_batches(B, orc):
+def test_forward_small_and_ragged_batches(B, path, orc):
     w = di.custom(f"small_b{B}", B, 13, 7, 1000, 64, 1, (13, 64, 64), hidden_top=(64, 32), cfg_id=13)
     inp = di.make_inputs(w)
-    _forward_check(inp, on_gpu(inp), orc)
+    _forward_check(inp, on_gpu(inp), orc, path=path)
 
 
-def test_forward_multi_hot_ragged_bags(orc):
+@pytest.mark.parametrize("path", ["fused", "layered"])
+def test_forward_multi_hot_ragged_bags(path, orc):
     w = di.custom("ragged_fwd", 211, 5, 9, 500, 32, 1, (5, 48, 32), hidden_top=(40,), cfg_id=14)
     inp = di.make_inputs(w)
     gen = torch.Generator().manual_seed(21)
@@ -353,16 +357,53 @@ def test_forward_multi_hot_ragged_bags(orc):
         off, n = di.ragged_bags(w.batch, 12, 1200 + t, empty_frac=0.25)
         inp.offsets[t] = off
         inp.indices[t] = torch.randint(0, w.rows, (n,), generator=gen)
-    _forward_check(inp, on_gpu(inp), orc)
+    _forward_check(inp, on_gpu(inp), orc, path=path)
 
 
-def test_forward_zero_last_layer_gives_exactly_half():
+@pytest.mark.parametrize("path", ["fused", "layered"])
+@pytest.mark.parametrize("ln_bot,hidden_top,D", [((13, 37, 16), (), 16), ((3, 300, 100, 48), (129, 17), 48),
+                                                 ((70, 1000, 256), (513, 96, 33), 256),
+                                                 ((13, 24, 20, 28, 32, 36, 40, 44, 52), (8,) * 7, 52)])
+def test_forward_odd_layer_shapes(ln_bot, hidden_top, D, path, orc):
+    """Widths that are not multiples of 4 or 16, K tails, a single top layer,
+    the widest row of the single-launch path and eight layers per MLP."""
+    w = di.custom(f"odd_{len(ln_bot)}_{D}", 77, ln_bot[0], 5, 900, D, 2, ln_bot, hidden_top=hidden_top, cfg_id=22)
+    inp = di.make_inputs(w)
+    _forward_check(inp, on_gpu(inp), orc, path=path)
+
+
+@pytest.mark.parametrize("path", ["fused", "layered"])
+def test_forward_zero_last_layer_gives_exactly_half(path):
     inp = di.make_inputs(di.PAGE4)
     inp.top_w[-1].zero_()
     inp.top_b[-1].zero_()
     g = on_gpu(inp)
-    out = dl.Model.from_inputs(g).forward(g.dense, g.indices, g.offsets)
+    out = dl.Model.from_inputs(g).forward(g.dense, g.indices, g.offsets, path=path)
     assert torch.all(out == 0.5)
+
+
+def test_forward_auto_path_choice():
+    """dlrm_forward takes the single launch for the page-4 model and the layered
+    path once the weights no longer fit in L2 (here 4 MB in one top layer)."""
+    g = on_gpu(di.make_inputs(di.PAGE4))
+    m = dl.Model.from_inputs(g)
+    auto = m.forward(g.dense, g.indices, g.offsets).clone()
+    assert torch.equal(auto, m.forward(g.dense, g.indices, g.offsets, path="fused"))
+    w = di.custom("big_top", 96, 13, 3, 1000, 64, 1, (13, 64), hidden_top=(1024, 1024), cfg_id=23)
+    g = on_gpu(di.make_inputs(w))
+    m = dl.Model.from_inputs(g)
+    auto = m.forward(g.dense, g.indices, g.offsets).clone()
+    assert torch.equal(auto, m.forward(g.dense, g.indices, g.offsets, path="layered"))
+
+
+@pytest.mark.parametrize("T,D", [(64, 64), (2, 1024), (40, 33), (3, 12)])
+def test_forward_fused_rejects_what_it_cannot_hold(T, D):
+    """Too much LDS (64 tables), rows past 256 or not a multiple of 4, rows under 16."""
+    w = di.custom(f"nofuse_{T}_{D}", 16, 5, T, 300, D, 1, (5, 16, D), hidden_top=(32,), cfg_id=24)
+    g = on_gpu(di.make_inputs(w))
+    with pytest.raises(dl.DlrmError) as e:
+        dl.Model.from_inputs(g).forward(g.dense, g.indices, g.offsets, path="fused")
+    assert e.value.code == dl.DLRM_E_UNSUPPORTED
 
 
 def test_forward_rejects_bad_shapes():
@@ -373,21 +414,22 @@ def test_forward_rejects_bad_shapes():
     assert e.value.code == dl.DLRM_E_SHAPE
 
 
-def test_forward_graph_capture_replays_match_eager():
+@pytest.mark.parametrize("path", ["fused", "layered"])
+def test_forward_graph_capture_replays_match_eager(path):
     inp = on_gpu(di.make_inputs(di.PAGE4))
     model = dl.Model.from_inputs(inp)
     B = inp.workload.batch
     out = torch.empty(B, device="cuda")
     ws = model.workspace(B)
     args = model.forward_args(inp.dense, inp.indices, inp.offsets)
-    model.forward(inp.dense, inp.indices, inp.offsets, out=out, workspace=ws, args=args)   # warm up
+    model.forward(inp.dense, inp.indices, inp.offsets, out=out, workspace=ws, args=args, path=path)   # warm up
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
         with torch.cuda.graph(graph, stream=s):
-            model.forward(inp.dense, inp.indices, inp.offsets, out=out, workspace=ws, args=args)
+            model.forward(inp.dense, inp.indices, inp.offsets, out=out, workspace=ws, args=args, path=path)
     torch.cuda.current_stream().wait_stream(s)
     gen = torch.Generator(device="cuda").manual_seed(3)
     for rep in range(4):
@@ -397,7 +439,7 @@ def test_forward_graph_capture_replays_match_eager():
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
-        eager = model.forward(inp.dense, inp.indices, inp.offsets)
+        eager = model.forward(inp.dense, inp.indices, inp.offsets, path=path)
         torch.cuda.synchronize()
         assert torch.equal(out, eager), f"replay {rep} differs"
 
@@ -528,10 +570,11 @@ def test_stacked_table_layout_is_bit_identical():
     a = dl.embbag_sum(inp.tables, inp.indices, inp.offsets)
     b = dl.embbag_sum(views, inp.indices, inp.offsets)
     assert torch.equal(a, b)
-    fa = dl.Model.from_inputs(inp).forward(inp.dense, inp.indices, inp.offsets).clone()
     sv = di.Inputs(w, inp.dense, views, inp.indices, inp.offsets, inp.bot_w, inp.bot_b, inp.top_w, inp.top_b)
-    fb = dl.Model.from_inputs(sv).forward(inp.dense, inp.indices, inp.offsets)
-    assert torch.equal(fa, fb)
+    for path in ("fused", "layered"):
+        fa = dl.Model.from_inputs(inp).forward(inp.dense, inp.indices, inp.offsets, path=path).clone()
+        fb = dl.Model.from_inputs(sv).forward(inp.dense, inp.indices, inp.offsets, path=path)
+        assert torch.equal(fa, fb)
 
 
 @pytest.mark.parametrize("T,D", [(64, 64), (2, 1024), (40, 33)])

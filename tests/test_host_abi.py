@@ -30,7 +30,8 @@ def lib():
 
 def test_header_declares_the_hot_path_calls():
     names = declared_functions()
-    for n in ("dlrm_embbag_sum", "dlrm_interact_lower_tri", "dlrm_linear_bias_act", "dlrm_forward"):
+    for n in ("dlrm_embbag_sum", "dlrm_interact_lower_tri", "dlrm_linear_bias_act", "dlrm_forward",
+              "dlrm_forward_fused", "dlrm_forward_layered"):
         assert n in names
 
 
@@ -54,7 +55,7 @@ def _model(ln_bot, ln_top, T, D, rows=100):
     fake = dl._vp * 64
     ptrs = fake(*([4096] * 64))  # never dereferenced: validation fails or only sizes are read
     m = dl._Model(len(ln_bot), ctypes.cast(keep[0], dl._i64p), len(ln_top), ctypes.cast(keep[1], dl._i64p), T, D,
-                  ctypes.cast(keep[2], dl._i64p), ptrs, ptrs, ptrs, ptrs, ptrs)
+                  ctypes.cast(keep[2], dl._i64p), ptrs, ptrs, ptrs, ptrs, ptrs, None)
     return m, (keep, ptrs)
 
 
@@ -90,7 +91,10 @@ def test_invalid_models_are_rejected(lib, ln_bot, ln_top, T, D, B):
     m, keep = _model(ln_bot, ln_top, T, D)
     assert lib.dlrm_forward_workspace_bytes(ctypes.byref(m), B) == 0
     one = dl._ptrs([])
-    rc = lib.dlrm_forward(ctypes.byref(m), B, 4096, one, dl._i64s([1] * T), one, 4096, 4096, 1 << 30, None)
+    for fn in (lib.dlrm_forward, lib.dlrm_forward_layered):
+        rc = fn(ctypes.byref(m), B, 4096, one, dl._i64s([1] * T), one, 4096, 4096, 1 << 30, None)
+        assert rc == dl.DLRM_E_SHAPE
+    rc = lib.dlrm_forward_fused(ctypes.byref(m), B, 4096, one, dl._i64s([1] * T), one, 4096, None)
     assert rc == dl.DLRM_E_SHAPE
 
 
@@ -110,6 +114,89 @@ def test_forward_rejects_missing_or_small_workspace(lib):
     assert lib.dlrm_forward(ctypes.byref(m), 16, 4096, fake, n, fake, 4096, 4096 + 16, need, None) == dl.DLRM_E_WORKSPACE
     assert lib.dlrm_forward(None, 16, 4096, fake, n, fake, 4096, 4096, need, None) == dl.DLRM_E_NULL
     assert lib.dlrm_forward(ctypes.byref(m), 16, None, fake, n, fake, 4096, 4096, need, None) == dl.DLRM_E_NULL
+
+
+def test_layered_forward_rejects_missing_or_small_workspace(lib):
+    m, keep = _model([13, 8, 4], [10, 8, 1], 3, 4)
+    need = lib.dlrm_forward_workspace_bytes(ctypes.byref(m), 16)
+    fake = (dl._vp * 3)(4096, 4096, 4096)
+    n = dl._i64s([16, 16, 16])
+    f = lib.dlrm_forward_layered
+    assert f(ctypes.byref(m), 16, 4096, fake, n, fake, 4096, None, need, None) == dl.DLRM_E_WORKSPACE
+    assert f(ctypes.byref(m), 16, 4096, fake, n, fake, 4096, 4096, need - 1, None) == dl.DLRM_E_WORKSPACE
+    assert f(ctypes.byref(m), 16, 4096, fake, n, fake, 4096, 4096 + 16, need, None) == dl.DLRM_E_WORKSPACE
+
+
+@pytest.mark.parametrize("ln_bot,ln_top,T,D,why", [
+    ([13, 8, 12], [18, 8, 1], 3, 12, "rows shorter than 16"),
+    ([13, 8, 33], [39, 8, 1], 3, 33, "rows not a multiple of 4"),
+    ([13, 8, 260], [266, 8, 1], 3, 260, "rows longer than 256"),
+    ([13] + [16] * 9, [22, 8, 1], 3, 16, "nine bottom layers"),
+    ([13, 8, 64], [64 + 2080, 8, 1], 64, 64, "LDS above 160 KiB"),
+])
+def test_fused_forward_rejects_models_outside_its_limits(lib, ln_bot, ln_top, T, D, why):
+    """Checked on the host before any launch, so no device is needed."""
+    m, keep = _model(ln_bot, ln_top, T, D)
+    fake = (dl._vp * T)(*([4096] * T))
+    n = dl._i64s([16] * T)
+    rc = lib.dlrm_forward_fused(ctypes.byref(m), 16, 4096, fake, n, fake, 4096, None)
+    assert rc == dl.DLRM_E_UNSUPPORTED, why
+
+
+def _packed_floats(ln):
+    n = 0
+    for k, o in zip(ln[:-1], ln[1:]):
+        f = ((o + 15) // 16) * ((k + 15) // 16) * 256
+        n += (f + 63) // 64 * 64
+    return n
+
+
+@pytest.mark.parametrize("ln_bot,ln_top,T,D", [
+    ([13, 512, 256, 64], [70, 512, 256, 1], 3, 64),
+    ([13, 512, 256, 64], [592, 512, 256, 1], 32, 64),
+    ([4, 32, 16], [22, 32, 1], 3, 16),
+    ([3, 37, 16], [22, 1], 3, 16),
+])
+def test_pack_weights_bytes_formula(lib, ln_bot, ln_top, T, D):
+    """Every layer but the one-output last: ceil(N/16) x ceil(K/16) tiles of 256
+    floats, each layer rounded up to 256 bytes."""
+    m, keep = _model(ln_bot, ln_top, T, D)
+    want = 4 * (_packed_floats(ln_bot) + _packed_floats(ln_top[:-1]))
+    assert lib.dlrm_pack_weights_bytes(ctypes.byref(m)) == want
+
+
+def test_pack_weights_argument_errors(lib):
+    m, keep = _model([13, 8, 16], [22, 8, 1], 3, 16)
+    need = lib.dlrm_pack_weights_bytes(ctypes.byref(m))
+    assert need > 0
+    f = lib.dlrm_pack_weights
+    assert f(None, 4096, need, None) == dl.DLRM_E_NULL
+    assert f(ctypes.byref(m), None, need, None) == dl.DLRM_E_NULL
+    assert f(ctypes.byref(m), 4096, need - 1, None) == dl.DLRM_E_WORKSPACE
+    assert f(ctypes.byref(m), 4096 + 16, need, None) == dl.DLRM_E_WORKSPACE
+    bad, keep2 = _model([13, 8, 12], [18, 8, 1], 3, 12)
+    assert lib.dlrm_pack_weights_bytes(ctypes.byref(bad)) == 0
+    assert f(ctypes.byref(bad), 4096, 1 << 20, None) == dl.DLRM_E_UNSUPPORTED
+
+
+def test_fused_forward_needs_packed_weights(lib):
+    m, keep = _model([13, 8, 16], [22, 8, 1], 3, 16)
+    fake = (dl._vp * 3)(4096, 4096, 4096)
+    n = dl._i64s([16, 16, 16])
+    assert lib.dlrm_forward_fused(ctypes.byref(m), 16, 4096, fake, n, fake, 4096, None) == dl.DLRM_E_NULL
+    m.packed_w = 4096 + 4
+    assert lib.dlrm_forward_fused(ctypes.byref(m), 16, 4096, fake, n, fake, 4096, None) == dl.DLRM_E_SHAPE
+
+
+def test_fused_forward_argument_errors(lib):
+    m, keep = _model([13, 8, 16], [22, 8, 1], 3, 16)
+    fake = (dl._vp * 3)(4096, 4096, 4096)
+    n = dl._i64s([16, 16, 16])
+    f = lib.dlrm_forward_fused
+    assert f(None, 16, 4096, fake, n, fake, 4096, None) == dl.DLRM_E_NULL
+    assert f(ctypes.byref(m), 16, None, fake, n, fake, 4096, None) == dl.DLRM_E_NULL
+    assert f(ctypes.byref(m), 16, 4096, fake, n, fake, None, None) == dl.DLRM_E_NULL
+    assert f(ctypes.byref(m), 0, 4096, fake, n, fake, 4096, None) == dl.DLRM_E_SHAPE
 
 
 def test_linear_argument_errors(lib):
