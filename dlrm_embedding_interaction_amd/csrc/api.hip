@@ -222,6 +222,27 @@ dlrm_status_t forward_args(const dlrm_model_t* m, int64_t batch, const float* de
                        multi_hot);
 }
 
+// Segments of the packed tail (see SmallBlock).
+void small_block(const dlrm_model_t* m, SmallBlock& sb) {
+    memset(&sb, 0, sizeof(sb));
+    const int klast = (int)m->ln_top[m->n_top - 2];
+    int off = 0;
+    auto add = [&](const float* src, int len, int pad_to) {
+        sb.src[sb.nseg] = src;
+        sb.len[sb.nseg] = len;
+        sb.off[sb.nseg] = off;
+        ++sb.nseg;
+        off += (pad_to + 3) / 4 * 4;
+    };
+    add(m->top_w ? m->top_w[m->n_top - 2] : nullptr, klast, klast);
+    add(m->top_b ? m->top_b[m->n_top - 2] : nullptr, 1, 4);
+    for (int32_t l = 0; l + 1 < m->n_bot && l < kFusedMaxLayers; ++l)
+        add(m->bot_b ? m->bot_b[l] : nullptr, (int)m->ln_bot[l + 1], (int)m->ln_bot[l + 1]);
+    for (int32_t l = 0; l + 2 < m->n_top && l < kFusedMaxLayers; ++l)
+        add(m->top_b ? m->top_b[l] : nullptr, (int)m->ln_top[l + 1], (int)m->ln_top[l + 1]);
+    sb.total = off;
+}
+
 // Kernel arguments of the single-launch path (with packed-weight pointers
 // relative to `packed`, which may be NULL when only the shape is checked);
 // false when the model is outside its limits.
@@ -245,8 +266,12 @@ bool fused_args(const dlrm_model_t* m, int64_t batch, const float* dense, float*
         fa.top.b[l] = m->top_b[l];
         off += packed_layer_floats(fa.top.dim[l + 1], fa.top.dim[l]);
     }
-    fa.last_w = m->top_w[m->n_top - 2];
-    fa.last_b = m->top_b[m->n_top - 2];
+    SmallBlock sb;
+    small_block(m, sb);
+    fa.small = packed ? packed + off : nullptr;
+    fa.n_small = sb.total;
+    fa.packed = packed;
+    fa.n_packed = (int64_t)off + sb.total;
     fa.dense = dense;
     fa.out = out;
     fa.B = batch;
@@ -255,12 +280,14 @@ bool fused_args(const dlrm_model_t* m, int64_t batch, const float* dense, float*
     return fused_supported(fa, aligned);
 }
 
-// Floats of the packed weights of every layer but the last.
+// Floats of the packed weights of every layer but the last, plus the tail.
 size_t packed_floats(const dlrm_model_t* m) {
     size_t n = 0;
     for (int32_t l = 0; l + 1 < m->n_bot; ++l) n += packed_layer_floats((int)m->ln_bot[l + 1], (int)m->ln_bot[l]);
     for (int32_t l = 0; l + 2 < m->n_top; ++l) n += packed_layer_floats((int)m->ln_top[l + 1], (int)m->ln_top[l]);
-    return n;
+    SmallBlock sb;
+    small_block(m, sb);
+    return n + ((size_t)sb.total + 63) / 64 * 64;
 }
 
 // Shape-only check of the single-launch path for a model (tables' alignment
@@ -365,8 +392,13 @@ DLRM_API dlrm_status_t dlrm_pack_weights(const dlrm_model_t* m, float* packed, s
     if (((uintptr_t)packed & 255u) != 0 || bytes < packed_floats(m) * sizeof(float)) return DLRM_E_WORKSPACE;
     for (int32_t l = 0; l + 1 < m->n_bot; ++l)
         if (!m->bot_w[l]) return DLRM_E_NULL;
-    for (int32_t l = 0; l + 2 < m->n_top; ++l)
+    for (int32_t l = 0; l + 1 < m->n_top; ++l)
         if (!m->top_w[l]) return DLRM_E_NULL;
+    if (!m->bot_b || !m->top_b) return DLRM_E_NULL;
+    for (int32_t l = 0; l + 1 < m->n_bot; ++l)
+        if (!m->bot_b[l]) return DLRM_E_NULL;
+    for (int32_t l = 0; l + 1 < m->n_top; ++l)
+        if (!m->top_b[l]) return DLRM_E_NULL;
     hipStream_t s = (hipStream_t)stream;
     size_t off = 0;
     for (int32_t l = 0; l + 1 < m->n_bot; ++l) {
@@ -379,6 +411,9 @@ DLRM_API dlrm_status_t dlrm_pack_weights(const dlrm_model_t* m, float* packed, s
         if (launch_pack_layer(m->top_w[l], N, K, packed + off, s) != hipSuccess) return DLRM_E_HIP;
         off += packed_layer_floats(N, K);
     }
+    SmallBlock sb;
+    small_block(m, sb);
+    if (launch_pack_small(sb, packed + off, s) != hipSuccess) return DLRM_E_HIP;
     return DLRM_OK;
 }
 

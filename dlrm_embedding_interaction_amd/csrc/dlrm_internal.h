@@ -35,8 +35,10 @@ struct MlpArgs {
 struct FusedArgs {
     TableArgs ta;
     MlpArgs bot, top;
-    const float* last_w;  // one-output last layer, nn.Linear layout (not packed)
-    const float* last_b;
+    const float* small;   // packed tail: last layer's weights and bias, hidden biases (small_block_floats)
+    int n_small;
+    const float* packed;  // start of the packed weights and their length in floats
+    int64_t n_packed;
     const float* dense;
     float* out;
     int64_t B;
@@ -92,6 +94,18 @@ hipError_t launch_fused_forward(FusedArgs fa, bool aligned16, bool multi_hot, hi
 // Floats of one packed (N, K) layer, rounded up to 256 bytes, and its packing.
 size_t packed_layer_floats(int N, int K);
 hipError_t launch_pack_layer(const float* W, int N, int K, float* packed, hipStream_t s);
+
+// The packed tail the single-launch kernel copies to LDS at its start: the
+// one-output last layer's weights (k_last floats, rounded up to 4), its bias
+// (4 floats), then the biases of every hidden layer (each rounded up to 4).
+struct SmallBlock {
+    const float* src[2 * kFusedMaxLayers + 2];
+    int len[2 * kFusedMaxLayers + 2];
+    int off[2 * kFusedMaxLayers + 2];
+    int nseg;
+    int total;  // floats, a multiple of 4
+};
+hipError_t launch_pack_small(const SmallBlock& sb, float* dst, hipStream_t s);
 
 hipError_t launch_check_indices(const CheckArgs& ca, int T, int64_t B, int32_t* bad, hipStream_t s);
 

@@ -45,6 +45,20 @@ __device__ __forceinline__ float lds_load(const float* p) { return *(const lds_f
 __device__ __forceinline__ void lds_store4(float* p, floatx4 v) { *(lds_floatx4*)(lds_float*)p = v; }
 __device__ __forceinline__ void lds_store(float* p, float v) { *(lds_float*)p = v; }
 
+// Raw buffer loads of the packed weights: a load whose offset lies past the
+// buffer's size returns zeros without a memory access, so a step past a
+// layer's last chunk still issues its loads (every wait keeps counting
+// exactly) but costs no cache traffic.  Word 3 of the resource is the gfx9
+// family's raw-buffer format.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t weight_rsrc(const float* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), (short)0, (int)bytes, 0x00020000);
+}
+constexpr uint32_t kOutOfRange = 0x7FFFFFF0u;
+__device__ __forceinline__ floatx4 buffer_load4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+    return __builtin_bit_cast(floatx4, v);
+}
+
 __device__ __forceinline__ float dpp_row_shr4(float v) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x114, 0xF, 0xF, false));
 }
@@ -84,8 +98,8 @@ __global__ __launch_bounds__(kBlock) void pack_layer_kernel(const float* __restr
     *reinterpret_cast<floatx4*>(packed + i * 4) = v;
 }
 
-// out[s][n] = act(sum_k in[s][k] W[n][k] + bias[n]) for s < S, n < N, with in
-// and out in LDS (row strides ldi, ldo) and W packed as above.  The N outputs
+// out[s][n] = act(sum_k in[s][k] W[n][k] + bias[n]) for s < S, n < N, with in,
+// out and bias in LDS (row strides ldi, ldo) and W packed as above.  The N outputs
 // form tiles of 16 features; wave w takes tiles w, w + NW, ... in passes of TW
 // tiles.  One step covers KU chunks of 16 k values; the weights of a step are
 // requested PD steps ahead into a register ring whose slots are fixed at
@@ -95,7 +109,7 @@ __global__ __launch_bounds__(kBlock) void pack_layer_kernel(const float* __restr
 // out[s][n] is zero for n in [N, round_up(N, 64)).
 template <int S, int TW, int KU, int PD>
 __device__ __forceinline__ void mlp_layer(const float* in, int ldi, int K, const float* __restrict__ Wp,
-                                          const float* __restrict__ bias, int N, bool relu, float* out, int ldo) {
+                                          const float* bias, int N, bool relu, float* out, int ldo) {
     constexpr int SG = S / 4;
     constexpr int NW = kFusedThreads / 64;
     const int lane = threadIdx.x & 63;
@@ -110,29 +124,34 @@ __device__ __forceinline__ void mlp_layer(const float* in, int ldi, int K, const
 #pragma unroll
     for (int sg = 0; sg < SG; ++sg) arow[sg] = in + (4 * sg + e) * ldi + 4 * kg;
 
+    const __amdgpu_buffer_rsrc_t wr = weight_rsrc(Wp, (uint32_t)ntile * nkc * 1024u);
     for (int t0 = 0; t0 < ntile; t0 += NW * TW) {
-        const float* wtile[TW];
+        uint32_t wtile[TW];  // byte offset of this lane's first chunk of each tile
         floatx4 acc[TW][SG];
         floatx4 bv[TW];
 #pragma unroll
         for (int u = 0; u < TW; ++u) {
-            // tiles past the last are read (clamped) but never stored
-            const int t = min(t0 + wave + NW * u, ntile - 1);
-            wtile[u] = Wp + ((int64_t)t * nkc * 64 + lane) * 4;
+            // tiles past the last read zeros and are never stored
+            const int t = t0 + wave + NW * u;
+            wtile[u] = t < ntile ? ((uint32_t)t * nkc * 64u + lane) * 16u : kOutOfRange;
             const int n0 = 16 * t + 4 * fg;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) bv[u][r] = bias[min(n0 + r, N - 1)];  // requested before the weights
+            for (int r = 0; r < 4; ++r) bv[u][r] = lds_load(bias + min(n0 + r, N - 1));  // staged in LDS
 #pragma unroll
             for (int sg = 0; sg < SG; ++sg) acc[u][sg] = floatx4{0.f, 0.f, 0.f, 0.f};
         }
         floatx4 ring[PD][TW][KU];
-        // chunks past the last are read (clamped) and meet zero activations
+        // Every step issues the same number of loads, so that each wait counts
+        // exactly its own step; chunks past the layer's last are out of range
+        // and read as zeros.
         auto loadw = [&](int kb, floatx4 (&w)[TW][KU]) {
 #pragma unroll
             for (int u = 0; u < TW; ++u)
 #pragma unroll
-                for (int c = 0; c < KU; ++c)
-                    w[u][c] = *reinterpret_cast<const floatx4*>(wtile[u] + min(kb * KU + c, nkc - 1) * 256);
+                for (int c = 0; c < KU; ++c) {
+                    const int ch = kb * KU + c;
+                    w[u][c] = buffer_load4(wr, ch < nkc ? wtile[u] + (uint32_t)ch * 1024u : kOutOfRange);
+                }
         };
         auto step = [&](int kb, const floatx4 (&w)[TW][KU]) {
             floatx4 a[KU][SG];
@@ -152,16 +171,17 @@ __device__ __forceinline__ void mlp_layer(const float* in, int ldi, int K, const
                                 __builtin_amdgcn_mfma_f32_4x4x1f32(w[u][c][q], a[c][sg][q], acc[u][sg], 0, 0, 0);
         };
 #pragma unroll
-        for (int p = 0; p < PD; ++p) loadw(min(p, nkb - 1), ring[p]);
+        for (int p = 0; p < PD; ++p) loadw(p, ring[p]);
         // whole trips of PD steps (a loop with a single exit, so the waits
-        // before each step count only that step's loads), then the rest
+        // before each step count only that step's loads), then the rest;
+        // refills past the last chunk are out of range
         const int trips = nkb / PD;
         for (int tr = 0; tr < trips; ++tr) {
 #pragma unroll
             for (int p = 0; p < PD; ++p) {
                 const int kb = tr * PD + p;
                 step(kb, ring[p]);
-                loadw(min(kb + PD, nkb - 1), ring[p]);
+                loadw(kb + PD, ring[p]);
             }
         }
         const int rest = nkb - trips * PD;
@@ -214,8 +234,14 @@ __device__ __forceinline__ void mlp_layer_any(const float* in, int ldi, int K, c
         mlp_layer<S, TW_, KU_, PD_>(in, ldi, K, Wp, bias, N, relu, out, ldo);   \
         return;                                                                 \
     }
-    if (tw <= 1) DLRM_LAYER(1, 4, 6)
+    const int nkc = (K + 15) >> 4;
+    // short rings for the short layers, so that few steps are padding
+    if (tw <= 1) {
+        if (nkc <= 16) DLRM_LAYER(1, 4, 4)
+        DLRM_LAYER(1, 4, 6)
+    }
     if (tw <= 2) DLRM_LAYER(2, 2, 6)
+    if (nkc <= 1) DLRM_LAYER(4, 1, 1)
     DLRM_LAYER(4, 1, 6)
 #undef DLRM_LAYER
 }
@@ -251,12 +277,27 @@ __global__ __launch_bounds__(kFusedThreads) void fused_forward_kernel(FusedArgs 
     float* const lds = reinterpret_cast<float*>(lds4);
     auto buf = [&](int i) { return lds + i * S * lda; };
     float* feat = lds + 2 * S * lda;
-    float* wlast = feat + S * F * LDR;
+    float* wlast = feat + S * F * LDR;  // the packed tail: last layer's weights and bias, hidden biases
     const int klast = fa.top.dim[fa.top.n_layers - 1];
+    float* bias_lds = wlast + ((klast + 3) & ~3) + 4;
+    const int nbot = fa.bot.n_layers;
+    const int ntop = fa.top.n_layers - 1;  // hidden top layers
     const int tid = threadIdx.x;
     const int64_t b0 = (int64_t)blockIdx.x * S;
     const int nb = (int)min((int64_t)S, fa.B - b0);
-    const float blast = fa.last_b[0];
+
+    // The L2 of every XCD starts each launch without the weights.  The blocks
+    // of one XCD (the hardware deals blocks to the 8 XCDs round-robin) first
+    // touch every 128-byte line of the packed weights once between them, so
+    // that each layer later streams from L2 rather than from the Infinity
+    // Cache; the touches complete while the bags are gathered.
+    float touch = 0.f;
+    {
+        const int64_t nlines = fa.n_packed >> 5;
+        const int64_t xblocks = max(1u, gridDim.x >> 3);
+        for (int64_t i = (int64_t)(blockIdx.x >> 3) * NT + tid; i < nlines; i += xblocks * NT)
+            touch += fa.packed[i << 5];
+    }
 
     // 0. zero both activation buffers (reads past a layer's K must be finite)
     for (int i = tid; i < (2 * S * lda) / 4; i += NT) lds4[i] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -269,7 +310,9 @@ __global__ __launch_bounds__(kFusedThreads) void fused_forward_kernel(FusedArgs 
         const int k = i - s * n0;
         lds_store(buf(0) + s * lda + k, fa.dense[(b0 + s) * n0 + k]);
     }
-    for (int k = tid; k < klast; k += NT) lds_store(wlast + k, fa.last_w[k]);
+    // one contiguous copy, so that no layer waits on a bias load later
+    for (int i = tid; i < (fa.n_small >> 2); i += NT)
+        lds_store4(wlast + 4 * i, *reinterpret_cast<const floatx4*>(fa.small + 4 * i));
 
     // 2. bags of this block's samples into feature rows 1..T
     {
@@ -298,9 +341,11 @@ __global__ __launch_bounds__(kFusedThreads) void fused_forward_kernel(FusedArgs 
 
     // 3. bottom MLP, ReLU after every layer
     int cur = 0;
-    for (int l = 0; l < fa.bot.n_layers; ++l) {
-        mlp_layer_any<S>(buf(cur), lda, fa.bot.dim[l], fa.bot.w[l], fa.bot.b[l], fa.bot.dim[l + 1], true,
+    int boff = 0;  // this layer's biases in bias_lds
+    for (int l = 0; l < nbot; ++l) {
+        mlp_layer_any<S>(buf(cur), lda, fa.bot.dim[l], fa.bot.w[l], bias_lds + boff, fa.bot.dim[l + 1], true,
                          buf(cur ^ 1), lda);
+        boff += (fa.bot.dim[l + 1] + 3) & ~3;
         __syncthreads();
         cur ^= 1;
     }
@@ -323,14 +368,15 @@ __global__ __launch_bounds__(kFusedThreads) void fused_forward_kernel(FusedArgs 
     cur ^= 1;
 
     // 6. top hidden layers with ReLU, 7. last layer with sigmoid
-    const int nt = fa.top.n_layers;
-    for (int l = 0; l + 1 < nt; ++l) {
-        mlp_layer_any<S>(buf(cur), lda, fa.top.dim[l], fa.top.w[l], fa.top.b[l], fa.top.dim[l + 1], true,
+    for (int l = 0; l < ntop; ++l) {
+        mlp_layer_any<S>(buf(cur), lda, fa.top.dim[l], fa.top.w[l], bias_lds + boff, fa.top.dim[l + 1], true,
                          buf(cur ^ 1), lda);
+        boff += (fa.top.dim[l + 1] + 3) & ~3;
         __syncthreads();
         cur ^= 1;
     }
-    last_layer<S>(buf(cur), lda, klast, wlast, blast, fa.out + b0, nb);
+    last_layer<S>(buf(cur), lda, klast, wlast, lds_load(wlast + ((klast + 3) & ~3)), fa.out + b0, nb);
+    asm volatile("; touched %0" ::"v"(touch));  // keeps the touch loads
 }
 
 // ---- host side ------------------------------------------------------------------
@@ -349,8 +395,23 @@ int fused_lda(const FusedArgs& fa) {
 
 size_t fused_lds_bytes(const FusedArgs& fa, int S) {
     const int F = fa.T + 1;
-    const int klast = fa.top.dim[fa.top.n_layers - 1];
-    return sizeof(float) * ((size_t)2 * S * fused_lda(fa) + (size_t)S * F * (fa.D + kRowPad) + klast);
+    return sizeof(float) * ((size_t)2 * S * fused_lda(fa) + (size_t)S * F * (fa.D + kRowPad) + fa.n_small);
+}
+
+// dst[i] for i < total: the segment of sb holding i, zero in the padding.
+__global__ __launch_bounds__(kBlock) void pack_small_kernel(SmallBlock sb, float* __restrict__ dst) {
+    const int i = blockIdx.x * kBlock + threadIdx.x;
+    if (i >= sb.total) return;
+    float v = 0.f;
+    for (int g = 0; g < sb.nseg; ++g)
+        if (i >= sb.off[g] && i < sb.off[g] + sb.len[g]) v = sb.src[g][i - sb.off[g]];
+    dst[i] = v;
+}
+
+hipError_t launch_pack_small(const SmallBlock& sb, float* dst, hipStream_t s) {
+    hipLaunchKernelGGL(pack_small_kernel, dim3((unsigned)((sb.total + kBlock - 1) / kBlock)), dim3(kBlock), 0, s, sb,
+                       dst);
+    return hipGetLastError();
 }
 
 template <int S, int G, int U, int R, int RT>

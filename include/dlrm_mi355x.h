@@ -78,10 +78,10 @@ typedef enum dlrm_status {
  *   bot_w[l]           (ln_bot[l+1], ln_bot[l]) nn.Linear layout, bot_b[l] (ln_bot[l+1])
  *   top_w[l]           (ln_top[l+1], ln_top[l]),                top_b[l] (ln_top[l+1])
  *   emb_w[t]           (rows[t], emb_dim)
- *   packed_w           NULL, or device memory holding the hidden-layer weights
+ *   packed_w           NULL, or device memory holding the weights and biases
  *                      in the order the single-launch forward reads them,
- *                      written by dlrm_pack_weights from the bot_w / top_w
- *                      above (pack again after changing them)
+ *                      written by dlrm_pack_weights from the arrays above
+ *                      (pack again after changing them)
  * Biases may not be NULL.
  */
 typedef struct dlrm_model {
@@ -301,7 +301,8 @@ dlrm_status_t dlrm_forward_layered(const dlrm_model_t* m, int64_t batch, const f
  * last layer is stored as tiles of 16 output features x 16 inputs, each tile
  * as 64 lanes x 4 floats in the operand order of the kernel's matrix-core
  * instruction, zero past the layer's edges, so that one wave reads 1 KiB of
- * contiguous memory per load.  packed: device, >= dlrm_pack_weights_bytes(m)
+ * contiguous memory per load.  A tail holds the last layer's weights and bias
+ * and every hidden layer's bias, which the kernel copies to LDS at once.  packed: device, >= dlrm_pack_weights_bytes(m)
  * bytes, 256-byte aligned; written asynchronously on `stream`.  The caller
  * stores the pointer in m->packed_w and packs again after changing weights.
  */
@@ -319,7 +320,8 @@ dlrm_status_t dlrm_pack_weights(const dlrm_model_t* m, float* packed, size_t byt
  * Returns DLRM_E_UNSUPPORTED, and enqueues nothing, unless emb_dim % 4 == 0,
  * 16 <= emb_dim <= 256, every table is 16-byte aligned, each MLP has at most 8
  * Linear layers and the block's LDS (2 x 8 x (widest layer rounded up to 64,
- * plus 8) + 8 x (T + 1) x (emb_dim + 4) + ln_top[n_top-2] floats) fits in
+ * plus 8) + 8 x (T + 1) x (emb_dim + 4) floats, plus the last layer's weights
+ * and every hidden layer's biases, each rounded up to 4 floats) fits in
  * 160 KiB.
  */
 dlrm_status_t dlrm_forward_fused(const dlrm_model_t* m, int64_t batch, const float* dense,

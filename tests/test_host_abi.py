@@ -159,9 +159,12 @@ def _packed_floats(ln):
 ])
 def test_pack_weights_bytes_formula(lib, ln_bot, ln_top, T, D):
     """Every layer but the one-output last: ceil(N/16) x ceil(K/16) tiles of 256
-    floats, each layer rounded up to 256 bytes."""
+    floats, each layer rounded up to 256 bytes; then the tail of the last
+    layer's weights and bias and the hidden biases, each rounded up to 4 floats."""
     m, keep = _model(ln_bot, ln_top, T, D)
-    want = 4 * (_packed_floats(ln_bot) + _packed_floats(ln_top[:-1]))
+    r4 = lambda v: (v + 3) // 4 * 4
+    tail = r4(ln_top[-2]) + 4 + sum(r4(n) for n in ln_bot[1:]) + sum(r4(n) for n in ln_top[1:-1])
+    want = 4 * (_packed_floats(ln_bot) + _packed_floats(ln_top[:-1]) + (tail + 63) // 64 * 64)
     assert lib.dlrm_pack_weights_bytes(ctypes.byref(m)) == want
 
 
