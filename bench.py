@@ -8,10 +8,15 @@ replayed from HIP graphs (captured once, outside the timed region) so that
 host launch overhead does not hide the kernels; --eager times plain calls.
 
 Printed: one JSON line with the contract fields, plus
-  roofline          the dominant kernel of a step against its roofline,
+  path              the path dlrm_forward takes for the workload: "fused"
+                    (the whole forward in one kernel) or "layered";
+  roofline          the dominant kernel of that path against its roofline,
                     from a live HIP-event timing of that kernel;
-  roofline_emb_interact  the same for the fused bag-gather + interaction kernel;
-  kernels           per-stage average durations (HIP events);
+  layered           the layered path's own dominant kernel and MLP rate, for
+                    reference (its kernels also serve as standalone calls);
+  roofline_emb_interact  the bag-gather + interaction kernel (dlrm_embbag_interact);
+  kernels           per-kernel average durations (HIP events): the
+                    single-launch forward and each stage of the layered path;
   cpu_baseline      the fp64 oracle timed on the host cores on a bounded
                     sample of the workload;
   secondary         the 32-table workload (bs 2048) when --secondary is given.
@@ -57,8 +62,24 @@ def parse():
     return p.parse_args()
 
 
+def fused_algorithmic(w):
+    """Algorithmic flops and HBM bytes of one single-launch forward: every
+    Linear layer and the dots; dense rows, gathered rows, indices, offsets,
+    the weights once and the outputs."""
+    B, T, D, L = w.batch, w.num_tables, w.dim, w.bag
+    flops = 2 * B * w.n_pairs * D
+    wbytes = 0
+    for ln in (list(w.ln_bot), list(w.ln_top)):
+        for K, N in zip(ln[:-1], ln[1:]):
+            flops += 2 * B * N * K
+            wbytes += 4 * (N * K + N)
+    nbytes = 4 * B * w.ln_bot[0] + B * T * L * (D * 4 + 8) + B * T * 8 + wbytes + 4 * B
+    return dict(name="fused_forward", kind="mfma", flops=flops, bytes=nbytes, M=B)
+
+
 def algorithmic(w):
-    """Algorithmic bytes / flops per launch of each stage (what the method must move or compute)."""
+    """Algorithmic bytes / flops per launch of each stage of the layered path
+    (what the method must move or compute)."""
     B, T, D, L = w.batch, w.num_tables, w.dim, w.bag
     P = w.n_pairs
     stages = []
@@ -102,6 +123,7 @@ def main():
     w = di.get(args.workload)
 
     res = run_workload(torch, dl, di, w, dev, args)
+    lay = res["layered"]
     out = {
         "metric": "DLRMv1 fwd µs @bs2048 nc=3/32; samples/s; emb-bag+interact HBM GB/s",
         "value": res["samples_per_s"],
@@ -119,10 +141,12 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "num_tables": w.num_tables, "rows_per_table": w.rows,
                    "dim": w.dim, "bag": w.bag, "ln_bot": list(w.ln_bot), "ln_top": list(w.ln_top),
                    "mode": "eager" if args.eager else "hip_graph", "index_sets": args.index_sets,
-                   "path": args.path},
+                   "path": res["path"]},
+        "path": res["path"],
         "us_per_forward_p10_p50_p90": [res["pct"]["p10"], res["pct"]["p50"], res["pct"]["p90"]],
         "us_per_forward_cold_p50": res["cold_us"],
         "roofline": res["roofline"],
+        "layered": lay,
         "roofline_emb_interact": res["roofline_emb"],
         "emb_interact_GBps": res["roofline_emb"]["achieved"],
         "mlp_TFLOPs": res["mlp_tflops"],
@@ -136,7 +160,7 @@ def main():
     if args.secondary:
         w2 = di.MANYTABLE
         r2 = run_workload(torch, dl, di, w2, dev, args)
-        out["secondary"] = {w2.name: {"us_per_forward": r2["ms_per_step"] * 1e3,
+        out["secondary"] = {w2.name: {"path": r2["path"], "us_per_forward": r2["ms_per_step"] * 1e3,
                                       "us_per_forward_p10_p50_p90": [r2["pct"]["p10"], r2["pct"]["p50"],
                                                                      r2["pct"]["p90"]],
                                       "us_per_forward_cold_p50": r2["cold_us"],
@@ -155,6 +179,7 @@ def run_workload(torch, dl, di, w, dev, args):
     inp = di.make_inputs(w, device=dev)
     model = dl.Model.from_inputs(inp)
     B = w.batch
+    path = model.path(B) if args.path == "auto" else args.path
     nsets = max(1, args.index_sets)
     idx_sets = [inp.indices]
     for s in range(1, nsets):
@@ -227,21 +252,36 @@ def run_workload(torch, dl, di, w, dev, args):
         cold = sorted(a.elapsed_time(b) * 1e3 for a, b in ct)[len(ct) // 2]
         del flush
 
-    kernels = time_stages(torch, dl, model, inp, idx_sets, ws, w, args.kernel_reps)
+    kernels = time_stages(torch, dl, model, inp, idx_sets, ws, w, args.kernel_reps,
+                          fused=model.packed is not None and path == "fused")
     traffic = counted_traffic(w.name)
-    roof = roofline(kernels, dominant=True, traffic=traffic)
-    roof_emb = roofline([k for k in kernels if k["name"] == "emb_interact"], dominant=True, traffic=traffic)
+    stages = [k for k in kernels if k["name"] != "fused_forward"]
+    roof_layered = roofline(stages, dominant=True, traffic=traffic)
+    roof_emb = roofline([k for k in stages if k["name"] == "emb_interact"], dominant=True, traffic=traffic)
+    if path == "fused":
+        fk = next(k for k in kernels if k["name"] == "fused_forward")
+        roof = roofline([fk], dominant=True, traffic=traffic)
+        roof["weights_streamed_per_block_bytes"] = int(model.packed.numel() * 4)
+        mlp_tf = fk["flops"] / (fk["us"] * 1e-6) / 1e12
+    else:
+        roof = roof_layered
     del inp, model, idx_sets, ws, argsets
     torch.cuda.empty_cache()
-    mlp = [k for k in kernels if k["name"] != "emb_interact"]
-    mlp_tf = sum(k["flops"] for k in mlp) / (sum(k["us"] for k in mlp) * 1e-6) / 1e12
+    mlp = [k for k in stages if k["name"] != "emb_interact"]
+    lay_tf = sum(k["flops"] for k in mlp) / (sum(k["us"] for k in mlp) * 1e-6) / 1e12
+    if path != "fused":
+        mlp_tf = lay_tf
+    layered = {"roofline": roof_layered, "mlp_TFLOPs": lay_tf,
+               "stage_us_sum": sum(k["us"] for k in stages)}
     return dict(ms_per_step=ms, samples_per_s=B / (ms * 1e-3), kernels=kernels, roofline=roof, roofline_emb=roof_emb,
-                pct=pct, cold_us=cold, mlp_tflops=mlp_tf)
+                pct=pct, cold_us=cold, mlp_tflops=mlp_tf, path=path, layered=layered)
 
 
-def time_stages(torch, dl, model, inp, idx_sets, ws, w, reps):
-    """Average duration of each stage's kernel, launched alone on the current stream, with HIP events."""
-    stages = algorithmic(w)
+def time_stages(torch, dl, model, inp, idx_sets, ws, w, reps, fused=False):
+    """Average duration of each kernel, launched alone on the current stream,
+    with HIP events: the single-launch forward (when `fused`) and every stage
+    of the layered path."""
+    stages = ([fused_algorithmic(w)] if fused else []) + algorithmic(w)
     B, D = w.batch, w.dim
     P = w.n_pairs
     ldR = (D + P + 3) // 4 * 4
@@ -268,6 +308,12 @@ def time_stages(torch, dl, model, inp, idx_sets, ws, w, reps):
         dl.embbag_interact(model.tables, idx_sets[cnt[0] % nsets], inp.offsets, R, concat_dense=False,
                            out=R[:, D:])
     calls["emb_interact"] = emb
+    yf = torch.empty(B, device=dev)
+
+    def fused_fwd():
+        cnt[0] += 1
+        model.forward(inp.dense, idx_sets[cnt[0] % nsets], inp.offsets, out=yf, path="fused")
+    calls["fused_forward"] = fused_fwd
     h = R[:, :D + P]
     for l, (W, b) in enumerate(zip(model.top_w, model.top_b)):
         last = l == len(model.top_w) - 1
@@ -392,7 +438,8 @@ def run_sweep(torch, dl, di, dev, args):
             a.steps, a.warmup = max(20, min(args.steps, 200)), 10
             r = run_workload(torch, dl, di, w, dev, a)
             emb = next(k for k in r["kernels"] if k["name"] == "emb_interact")
-            row = dict(batch=B, tables=T, us_per_forward=r["ms_per_step"] * 1e3, samples_per_s=r["samples_per_s"],
+            row = dict(batch=B, tables=T, path=r["path"], us_per_forward=r["ms_per_step"] * 1e3,
+                       samples_per_s=r["samples_per_s"],
                        emb_interact_us=emb["us"], emb_interact_GBps=r["roofline_emb"]["achieved"],
                        kernels={k["name"]: k["us"] for k in r["kernels"]})
             rows.append(row)

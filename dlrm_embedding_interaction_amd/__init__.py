@@ -99,6 +99,8 @@ def load(build_if_missing: bool = True) -> ctypes.CDLL:
     L.dlrm_forward.argtypes = [ctypes.POINTER(_Model), ctypes.c_int64, _vp, ctypes.POINTER(_vp), _i64p,
                                ctypes.POINTER(_vp), _vp, _vp, ctypes.c_size_t, _vp]
     L.dlrm_forward_layered.argtypes = L.dlrm_forward.argtypes
+    L.dlrm_forward_path.argtypes = [ctypes.POINTER(_Model), ctypes.c_int64]
+    L.dlrm_forward_path.restype = ctypes.c_int32
     L.dlrm_pack_weights_bytes.argtypes = [ctypes.POINTER(_Model)]
     L.dlrm_pack_weights_bytes.restype = ctypes.c_size_t
     L.dlrm_pack_weights.argtypes = [ctypes.POINTER(_Model), _vp, ctypes.c_size_t, _vp]
@@ -350,8 +352,15 @@ class Model:
         return True
 
     @classmethod
-    def from_inputs(cls, inp) -> "Model":
-        return cls(inp.tables, inp.bot_w, inp.bot_b, inp.top_w, inp.top_b, n_dense=inp.workload.n_dense)
+    def from_inputs(cls, inp, pack: bool = True) -> "Model":
+        return cls(inp.tables, inp.bot_w, inp.bot_b, inp.top_w, inp.top_b, n_dense=inp.workload.n_dense, pack=pack)
+
+    def path(self, batch: int) -> str:
+        """The path dlrm_forward takes for `batch` samples: "fused" or "layered"."""
+        p = load().dlrm_forward_path(ctypes.byref(self._desc), int(batch))
+        if p == 0:
+            raise DlrmError(DLRM_E_SHAPE, "dlrm_forward_path", "invalid model or batch")
+        return "fused" if p == 2 else "layered"
 
     def workspace_bytes(self, batch: int) -> int:
         n = load().dlrm_forward_workspace_bytes(ctypes.byref(self._desc), int(batch))

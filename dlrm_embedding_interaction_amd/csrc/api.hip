@@ -302,11 +302,22 @@ bool model_fits_fused(const dlrm_model_t* m) {
     return fused_args(m, 1, nullptr, nullptr, ta, aligned, nullptr, fa);
 }
 
-// dlrm_forward takes the single-launch path up to this batch and while the
-// Linear weights stay well inside one XCD's 4 MiB L2 (every block streams all
-// of them).
-constexpr int64_t kFusedAutoMaxBatch = 16384;
+// Where dlrm_forward takes the single launch.  Every block streams all the
+// Linear weights from L2 (so they must stay well inside one XCD's 4 MiB), and
+// one block holds 8 samples, so a forward costs about one block's time per
+// 2048 samples; the layered GEMMs share weights across the whole chip.
+// Measured on MI355X (batch x tables sweep of the 13-512-256-64 /
+// (64+P)-512-256-1 model): the single launch is faster up to batch 4096,
+// except with 32 tables below batch 1024, where gathering 32 bags and
+// streaming the 592-wide first top layer per block costs more than the
+// layered path's launches.
+constexpr int64_t kFusedAutoMaxBatch = 4096;
 constexpr int64_t kFusedAutoMaxWeightBytes = 3 << 20;
+bool fused_preferred(const dlrm_model_t* m, int64_t batch) {
+    if (batch > kFusedAutoMaxBatch) return false;
+    if (m->num_tables >= 24 && batch < 1024) return false;
+    return true;
+}
 
 // Bytes of all Linear weights of the model.
 int64_t weight_bytes(const dlrm_model_t* m) {
@@ -431,6 +442,14 @@ DLRM_API dlrm_status_t dlrm_forward_fused(const dlrm_model_t* m, int64_t batch, 
     return from_hip(launch_fused_forward(fa, aligned, multi_hot, (hipStream_t)stream));
 }
 
+DLRM_API int32_t dlrm_forward_path(const dlrm_model_t* m, int64_t batch) {
+    if (!m || validate_model(m, batch) != DLRM_OK) return 0;
+    if (m->packed_w && al16(m->packed_w) && fused_preferred(m, batch) &&
+        weight_bytes(m) <= kFusedAutoMaxWeightBytes && model_fits_fused(m))
+        return DLRM_PATH_FUSED;
+    return DLRM_PATH_LAYERED;
+}
+
 DLRM_API dlrm_status_t dlrm_forward(const dlrm_model_t* m, int64_t batch, const float* dense,
                                     const int64_t* const* indices, const int64_t* n_indices,
                                     const int64_t* const* offsets, float* out, void* workspace, size_t ws_bytes,
@@ -443,7 +462,7 @@ DLRM_API dlrm_status_t dlrm_forward(const dlrm_model_t* m, int64_t batch, const 
     make_plan(m, batch, &p);
     if (!workspace || ((uintptr_t)workspace & 255u) != 0 || ws_bytes < p.total) return DLRM_E_WORKSPACE;
     FusedArgs fa;
-    if (m->packed_w && al16(m->packed_w) && batch <= kFusedAutoMaxBatch &&
+    if (m->packed_w && al16(m->packed_w) && fused_preferred(m, batch) &&
         weight_bytes(m) <= kFusedAutoMaxWeightBytes && fused_args(m, batch, dense, out, ta, aligned, m->packed_w, fa))
         return from_hip(launch_fused_forward(fa, aligned, multi_hot, (hipStream_t)stream));
     return forward_layered(m, batch, dense, out, ta, aligned, multi_hot, workspace, ws_bytes, (hipStream_t)stream);

@@ -269,16 +269,26 @@ size_t dlrm_forward_workspace_bytes(const dlrm_model_t* m, int64_t batch);
  *   out        device (B) fp32 probabilities
  *   workspace  device, >= dlrm_forward_workspace_bytes(m, B), 256-byte aligned
  * Enqueues either one kernel (the single-launch path of dlrm_forward_fused,
- * taken when m->packed_w is set, the model fits that path and its weights are
- * small enough to stay in L2) or a few kernels (dlrm_forward_layered) on
- * `stream`; the workspace must
- * not be used by another call until they finish.  Both paths compute the same
- * function; results agree to rounding.
+ * taken when m->packed_w is set, the model fits that path, its Linear weights
+ * take at most 3 MiB and the batch is at most 4096 -- at least 1024 with 24
+ * tables or more -- where it measured faster) or a few kernels
+ * (dlrm_forward_layered) on `stream`; the workspace must not be used by
+ * another call until they finish.  Both paths compute the same function;
+ * results agree to rounding.
  */
 dlrm_status_t dlrm_forward(const dlrm_model_t* m, int64_t batch, const float* dense,
                            const int64_t* const* indices, const int64_t* n_indices,
                            const int64_t* const* offsets, float* out, void* workspace,
                            size_t ws_bytes, void* stream);
+
+/*
+ * dlrm_forward_path -- which path dlrm_forward takes for model m and `batch`
+ * samples: DLRM_PATH_FUSED (one launch), DLRM_PATH_LAYERED, or 0 when m or
+ * batch is invalid.  Host only.
+ */
+#define DLRM_PATH_LAYERED 1
+#define DLRM_PATH_FUSED 2
+int32_t dlrm_forward_path(const dlrm_model_t* m, int64_t batch);
 
 /*
  * dlrm_forward_layered -- dlrm_forward as a sequence of kernels: one MFMA

@@ -383,17 +383,26 @@ def test_forward_zero_last_layer_gives_exactly_half(path):
 
 
 def test_forward_auto_path_choice():
-    """dlrm_forward takes the single launch for the page-4 model and the layered
-    path once the weights no longer fit in L2 (here 4 MB in one top layer)."""
+    """dlrm_forward takes the single launch for the page-4 model, and the layered
+    path once the weights no longer fit in L2 (here 4 MB in one top layer), past
+    batch 4096, for 32 tables below batch 1024, or without packed weights."""
     g = on_gpu(di.make_inputs(di.PAGE4))
     m = dl.Model.from_inputs(g)
     auto = m.forward(g.dense, g.indices, g.offsets).clone()
     assert torch.equal(auto, m.forward(g.dense, g.indices, g.offsets, path="fused"))
-    w = di.custom("big_top", 96, 13, 3, 1000, 64, 1, (13, 64), hidden_top=(1024, 1024), cfg_id=23)
-    g = on_gpu(di.make_inputs(w))
-    m = dl.Model.from_inputs(g)
-    auto = m.forward(g.dense, g.indices, g.offsets).clone()
-    assert torch.equal(auto, m.forward(g.dense, g.indices, g.offsets, path="layered"))
+    unpacked = dl.Model.from_inputs(g, pack=False)
+    assert torch.equal(unpacked.forward(g.dense, g.indices, g.offsets),
+                       m.forward(g.dense, g.indices, g.offsets, path="layered"))
+    with pytest.raises(dl.DlrmError) as e:
+        unpacked.forward(g.dense, g.indices, g.offsets, path="fused")
+    assert e.value.code == dl.DLRM_E_NULL
+    cases = [di.custom("big_top", 96, 13, 3, 1000, 64, 1, (13, 64), hidden_top=(1024, 1024), cfg_id=23),
+             di.sweep(8192, 1), di.sweep(512, 32)]
+    for w in cases:
+        g = on_gpu(di.make_inputs(w))
+        m = dl.Model.from_inputs(g)
+        auto = m.forward(g.dense, g.indices, g.offsets).clone()
+        assert torch.equal(auto, m.forward(g.dense, g.indices, g.offsets, path="layered")), w.name
 
 
 @pytest.mark.parametrize("T,D", [(64, 64), (2, 1024), (40, 33), (3, 12)])

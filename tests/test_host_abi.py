@@ -182,6 +182,26 @@ def test_pack_weights_argument_errors(lib):
     assert f(ctypes.byref(bad), 4096, 1 << 20, None) == dl.DLRM_E_UNSUPPORTED
 
 
+def test_forward_path_choice(lib):
+    """Layered without packed weights; single launch with them up to batch 4096
+    (from 1024 with 24+ tables); 0 for invalid input.  Host only."""
+    m, keep = _model([13, 512, 256, 64], [70, 512, 256, 1], 3, 64)
+    assert lib.dlrm_forward_path(ctypes.byref(m), 2048) == 1
+    m.packed_w = 4096
+    assert lib.dlrm_forward_path(ctypes.byref(m), 2048) == 2
+    assert lib.dlrm_forward_path(ctypes.byref(m), 4096) == 2
+    assert lib.dlrm_forward_path(ctypes.byref(m), 4097) == 1
+    assert lib.dlrm_forward_path(ctypes.byref(m), 0) == 0
+    assert lib.dlrm_forward_path(None, 16) == 0
+    m32, keep32 = _model([13, 512, 256, 64], [64 + 528, 512, 256, 1], 32, 64)
+    m32.packed_w = 4096
+    assert lib.dlrm_forward_path(ctypes.byref(m32), 512) == 1
+    assert lib.dlrm_forward_path(ctypes.byref(m32), 1024) == 2
+    big, keep3 = _model([13, 64], [70, 1024, 1024, 1], 3, 64)
+    big.packed_w = 4096
+    assert lib.dlrm_forward_path(ctypes.byref(big), 64) == 1   # 5 MB of weights
+
+
 def test_fused_forward_needs_packed_weights(lib):
     m, keep = _model([13, 8, 16], [22, 8, 1], 3, 16)
     fake = (dl._vp * 3)(4096, 4096, 4096)
