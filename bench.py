@@ -5,7 +5,10 @@ top MLP, sigmoid) over one batch of seeded synthetic inputs already resident
 in HBM.  Steps cycle through --index-sets independently drawn index sets so
 that consecutive steps gather different rows.  By default the steps are
 replayed from HIP graphs (captured once, outside the timed region) so that
-host launch overhead does not hide the kernels; --eager times plain calls.
+host launch overhead does not hide the kernels: the timed run replays graphs
+of --graph-steps consecutive steps (one graph launch per 8 forwards, as a
+serving loop would), the percentiles and the cold-cache figure time single
+steps, and --eager times plain calls.
 
 Printed: one JSON line with the contract fields, plus
   path              the path dlrm_forward takes for the workload: "fused"
@@ -47,6 +50,8 @@ def parse():
     p.add_argument("--workload", default="page4")
     p.add_argument("--index-sets", type=int, default=8)
     p.add_argument("--eager", action="store_true", help="time plain calls instead of graph replays")
+    p.add_argument("--graph-steps", type=int, default=8,
+                   help="consecutive steps (cycling the index sets) captured in one HIP graph for the timed run")
     p.add_argument("--path", default="auto", choices=["auto", "fused", "layered"],
                    help="dlrm_forward (auto), dlrm_forward_fused or dlrm_forward_layered")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -141,6 +146,7 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "num_tables": w.num_tables, "rows_per_table": w.rows,
                    "dim": w.dim, "bag": w.bag, "ln_bot": list(w.ln_bot), "ln_top": list(w.ln_top),
                    "mode": "eager" if args.eager else "hip_graph", "index_sets": args.index_sets,
+                   "steps_per_graph": 1 if args.eager else max(1, min(args.graph_steps, args.steps)),
                    "path": res["path"]},
         "path": res["path"],
         "us_per_forward_p10_p50_p90": [res["pct"]["p10"], res["pct"]["p50"], res["pct"]["p90"]],
@@ -213,13 +219,31 @@ def run_workload(torch, dl, di, w, dev, args):
         def run(i):
             graphs[i % nsets].replay()
 
+        # the timed run replays graphs of G consecutive steps, so that one
+        # graph launch covers G forwards (the serving loop's form)
+        G = max(1, min(args.graph_steps, args.steps))
+        multi = torch.cuda.CUDAGraph()
+        stream.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(stream):
+            with torch.cuda.graph(multi, stream=stream):
+                for i in range(G):
+                    step(i)
+        torch.cuda.current_stream().wait_stream(stream)
+        torch.cuda.synchronize()
+
     for i in range(args.warmup):
         run(i)
     torch.cuda.synchronize()
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        run(i)
+    if args.eager:
+        for i in range(args.steps):
+            run(i)
+    else:
+        for _ in range(args.steps // G):
+            multi.replay()
+        for i in range(args.steps % G):
+            run(i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms = (t1 - t0) * 1e3 / args.steps
