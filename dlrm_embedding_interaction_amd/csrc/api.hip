@@ -303,19 +303,21 @@ bool model_fits_fused(const dlrm_model_t* m) {
 }
 
 // Where dlrm_forward takes the single launch.  Every block streams all the
-// Linear weights from L2 (so they must stay well inside one XCD's 4 MiB), and
-// one block holds 8 samples, so a forward costs about one block's time per
-// 2048 samples; the layered GEMMs share weights across the whole chip.
-// Measured on MI355X (batch x tables sweep of the 13-512-256-64 /
-// (64+P)-512-256-1 model): the single launch is faster up to batch 4096,
-// except with 32 tables below batch 1024, where gathering 32 bags and
-// streaming the 592-wide first top layer per block costs more than the
-// layered path's launches.
-constexpr int64_t kFusedAutoMaxBatch = 4096;
+// Linear weights from L2 (so they must stay well inside one XCD's 4 MiB),
+// and a block holds 8 samples (16 past batch 2048), so a forward costs about
+// one block's time per round of 256 blocks; the layered GEMMs share weights
+// across the whole chip.  Measured on MI355X over the batch x tables sweep
+// of the 13-512-256-64 / (64+P)-512-256-1 model (both paths replayed from
+// graphs of 8 steps): the single launch is faster up to batch 8192 with up
+// to 8 tables, from batch 512 with 16 tables, and only from 1024 to 2048 with
+// 32 tables, where gathering 32 bags and streaming the 592-wide first top
+// layer per block dominate.
+constexpr int64_t kFusedAutoMaxBatch = 8192;
 constexpr int64_t kFusedAutoMaxWeightBytes = 3 << 20;
 bool fused_preferred(const dlrm_model_t* m, int64_t batch) {
     if (batch > kFusedAutoMaxBatch) return false;
-    if (m->num_tables >= 24 && batch < 1024) return false;
+    if (m->num_tables >= 24) return batch >= 1024 && batch <= 2048;
+    if (m->num_tables >= 12) return batch >= 512;
     return true;
 }
 

@@ -240,9 +240,15 @@ __device__ __forceinline__ void mlp_layer_any(const float* in, int ldi, int K, c
         if (nkc <= 16) DLRM_LAYER(1, 4, 4)
         DLRM_LAYER(1, 4, 6)
     }
-    if (tw <= 2) DLRM_LAYER(2, 2, 6)
-    if (nkc <= 1) DLRM_LAYER(4, 1, 1)
-    DLRM_LAYER(4, 1, 6)
+    if constexpr (S > 8) {
+        // 16 samples: two tiles per wave and pass at most (registers)
+        if (nkc <= 1) DLRM_LAYER(2, 1, 1)
+        DLRM_LAYER(2, 2, 6)
+    } else {
+        if (tw <= 2) DLRM_LAYER(2, 2, 6)
+        if (nkc <= 1) DLRM_LAYER(4, 1, 1)
+        DLRM_LAYER(4, 1, 6)
+    }
 #undef DLRM_LAYER
 }
 
@@ -449,17 +455,24 @@ bool fused_supported(const FusedArgs& fa, bool aligned16) {
     return fused_lds_bytes(fa, kFusedSamples) <= kFusedMaxLds;
 }
 
-hipError_t launch_fused_forward(FusedArgs fa, bool aligned16, bool multi_hot, hipStream_t s) {
-    if (!fused_supported(fa, aligned16)) return hipErrorInvalidValue;
-    fa.lda = fused_lda(fa);
+// Samples per block: 8 while the batch fills at most one round of blocks
+// (one per CU), 16 beyond that when the LDS allows -- a block's time is set
+// by streaming every weight once, so fewer, fuller blocks win once the
+// batch needs several rounds (the matrix cores then set the pace).
+int fused_samples(const FusedArgs& fa) {
+    if (fa.B > 2048 && fused_lds_bytes(fa, 16) <= kFusedMaxLds) return 16;
+    return kFusedSamples;
+}
+
+template <int S>
+static hipError_t launch_fused_s(FusedArgs& fa, bool multi_hot, hipStream_t s) {
     const int F = fa.T + 1;
     const int n4 = (F - 1 + 3) / 4;
-    const int items = kFusedSamples * n4 * (n4 + 1) / 2;
+    const int items = S * n4 * (n4 + 1) / 2;
     int dsplit = 1;
     while (dsplit < 4 && items * dsplit * 2 <= kFusedThreads && fa.D % (4 * dsplit * 2) == 0) dsplit *= 2;
     fa.dsplit = dsplit;
     const int g = pow2_at_least((fa.D + 3) / 4);
-    constexpr int S = kFusedSamples;
 #define FUSED_G(G_)                                                                                 \
     case G_:                                                                                        \
         if (F <= 12) {                                                                              \
@@ -477,6 +490,13 @@ hipError_t launch_fused_forward(FusedArgs fa, bool aligned16, bool multi_hot, hi
         default: return hipErrorInvalidValue;
     }
 #undef FUSED_G
+}
+
+hipError_t launch_fused_forward(FusedArgs fa, bool aligned16, bool multi_hot, hipStream_t s) {
+    if (!fused_supported(fa, aligned16)) return hipErrorInvalidValue;
+    fa.lda = fused_lda(fa);
+    if (fused_samples(fa) == 16) return launch_fused_s<16>(fa, multi_hot, s);
+    return launch_fused_s<8>(fa, multi_hot, s);
 }
 
 }  // namespace dlrm

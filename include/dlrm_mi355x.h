@@ -270,9 +270,9 @@ size_t dlrm_forward_workspace_bytes(const dlrm_model_t* m, int64_t batch);
  *   workspace  device, >= dlrm_forward_workspace_bytes(m, B), 256-byte aligned
  * Enqueues either one kernel (the single-launch path of dlrm_forward_fused,
  * taken when m->packed_w is set, the model fits that path, its Linear weights
- * take at most 3 MiB and the batch is at most 4096 -- at least 1024 with 24
- * tables or more -- where it measured faster) or a few kernels
- * (dlrm_forward_layered) on `stream`; the workspace must not be used by
+ * take at most 3 MiB and the batch is where it measured faster: at most 8192
+ * with fewer than 12 tables, 512..8192 with 12 to 23 tables, 1024..2048 with
+ * 24 or more) or a few kernels (dlrm_forward_layered) on `stream`; the workspace must not be used by
  * another call until they finish.  Both paths compute the same function;
  * results agree to rounding.
  */
@@ -323,8 +323,9 @@ dlrm_status_t dlrm_pack_weights(const dlrm_model_t* m, float* packed, size_t byt
  * dlrm_forward_fused -- dlrm_forward in a single kernel launch, the pages'
  * "one kernel per forward" design (dlrm_megakernel.rs module doc and
  * cuda_source steps 1-7 on "luminal compare dlrm-fused-kernels...
- * dlrm-pt2-megakernel").  Each block carries 8 samples through the whole
- * network with its activations in LDS and the packed weights (m->packed_w,
+ * dlrm-pt2-megakernel").  Each block carries 8 samples (16 beyond batch 2048
+ * when they fit) through the whole network with its activations in LDS and
+ * the packed weights (m->packed_w,
  * DLRM_E_NULL when absent) read from L2; no workspace is used.  Arguments as
  * dlrm_forward without the workspace.
  * Returns DLRM_E_UNSUPPORTED, and enqueues nothing, unless emb_dim % 4 == 0,

@@ -183,20 +183,26 @@ def test_pack_weights_argument_errors(lib):
 
 
 def test_forward_path_choice(lib):
-    """Layered without packed weights; single launch with them up to batch 4096
-    (from 1024 with 24+ tables); 0 for invalid input.  Host only."""
+    """Layered without packed weights; with them the single launch up to batch
+    8192 (from 512 with 12-23 tables, 1024..2048 with 24+); 0 for invalid
+    input.  Host only."""
     m, keep = _model([13, 512, 256, 64], [70, 512, 256, 1], 3, 64)
     assert lib.dlrm_forward_path(ctypes.byref(m), 2048) == 1
     m.packed_w = 4096
     assert lib.dlrm_forward_path(ctypes.byref(m), 2048) == 2
-    assert lib.dlrm_forward_path(ctypes.byref(m), 4096) == 2
-    assert lib.dlrm_forward_path(ctypes.byref(m), 4097) == 1
+    assert lib.dlrm_forward_path(ctypes.byref(m), 8192) == 2
+    assert lib.dlrm_forward_path(ctypes.byref(m), 8193) == 1
     assert lib.dlrm_forward_path(ctypes.byref(m), 0) == 0
     assert lib.dlrm_forward_path(None, 16) == 0
+    m16, keep16 = _model([13, 512, 256, 64], [64 + 136, 512, 256, 1], 16, 64)
+    m16.packed_w = 4096
+    assert lib.dlrm_forward_path(ctypes.byref(m16), 256) == 1
+    assert lib.dlrm_forward_path(ctypes.byref(m16), 512) == 2
     m32, keep32 = _model([13, 512, 256, 64], [64 + 528, 512, 256, 1], 32, 64)
     m32.packed_w = 4096
     assert lib.dlrm_forward_path(ctypes.byref(m32), 512) == 1
     assert lib.dlrm_forward_path(ctypes.byref(m32), 1024) == 2
+    assert lib.dlrm_forward_path(ctypes.byref(m32), 4096) == 1
     big, keep3 = _model([13, 64], [70, 1024, 1024, 1], 3, 64)
     big.packed_w = 4096
     assert lib.dlrm_forward_path(ctypes.byref(big), 64) == 1   # 5 MB of weights
