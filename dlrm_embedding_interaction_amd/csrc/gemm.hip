@@ -8,12 +8,18 @@
 // nvidia-devcontainer-args...perf/compile-write-rayon").
 //
 // Both operands are K-contiguous ("NT"), so a tile of each is staged in LDS as
-// [row][k] with 4 floats of padding per row.  A wave owns a (TM*16) x (TN*16)
-// sub-tile built from v_mfma_f32_16x16x4f32 blocks; for every 16-wide k slice
-// each lane reads one float4 of A and one of B from LDS and feeds their
-// four components to four MFMAs (lane l supplies A[l%16][k] and B[k][l%16]
-// with k = 4*(l/16) + q for MFMA q, a permutation of the k order that both
-// operands share).  Two LDS buffers alternate between k tiles and two
+// [row][k] with 4 floats of padding per row.  A wave owns a (TM*MF) x (TN*MF)
+// sub-tile built from MF x MF MFMA blocks:
+//  * MF = 16, v_mfma_f32_16x16x4f32: for every 16-wide k slice each lane
+//    reads one float4 of A and one of B from LDS and feeds their four
+//    components to four MFMAs (lane l supplies A[l%16][k] and B[k][l%16] with
+//    k = 4*(l/16) + q for MFMA q);
+//  * MF = 32, v_mfma_f32_32x32x2f32 (the full-rate fp32 shape on gfx950):
+//    each lane reads two float4 of A and two of B per 16-wide k slice and
+//    feeds them to eight MFMAs (lane l supplies A[l%32][k] and B[k][l%32]
+//    with k = 8*(l/32) + q for MFMA q).
+// Either way the k order is a permutation that both operands share.  Two LDS
+// buffers alternate between k tiles and two
 // register stages hold the next two tiles in flight: while tile c is
 // multiplied from one buffer, tile c+1 (fetched one tile earlier) is stored to
 // the other and tile c+3 is requested, so each k tile costs one barrier and
@@ -34,15 +40,31 @@ __device__ __forceinline__ float apply_act(float v, int act) {
     return v;
 }
 
-template <int BM, int BN, int BK, int WM, int WN, bool VA, bool VB>
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+template <int MF>
+struct MfmaAcc;
+template <>
+struct MfmaAcc<16> {
+    typedef floatx4 T;
+};
+template <>
+struct MfmaAcc<32> {
+    typedef floatx16 T;
+};
+
+template <int BM, int BN, int BK, int WM, int WN, int MF, bool VA, bool VB>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_bias_act_kernel(int M, int N, int K, const float* __restrict__ A,
                                                                     int64_t lda, const float* __restrict__ W,
                                                                     const float* __restrict__ bias, int act,
                                                                     float* __restrict__ Y, int64_t ldy, int tiles_m,
                                                                     int tiles_n, bool vec_y) {
+    static_assert(MF == 16 || MF == 32, "16x16x4 or 32x32x2 blocks");
+    using Acc = typename MfmaAcc<MF>::T;
+    constexpr int NR = MF * MF / 64;  // accumulator values per lane and block
     constexpr int NT = WM * WN * 64;
-    constexpr int TM = BM / (WM * 16);
-    constexpr int TN = BN / (WN * 16);
+    constexpr int TM = BM / (WM * MF);
+    constexpr int TN = BN / (WN * MF);
     constexpr int LDK = BK + 4;
     static_assert(BK % 16 == 0, "BK must be a multiple of 16");
     static_assert(TM >= 1 && TN >= 1, "wave tile too small");
@@ -52,10 +74,11 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bias_act_kernel(int M, int N
     static_assert((VA ? A_V * 4 : A_V) * NT == BM * BK, "A tile must split evenly");
     static_assert((VB ? B_V * 4 : B_V) * NT == BN * BK, "B tile must split evenly");
 
-    // two A buffers, two B buffers; reused at the end to stage the output tile
+    // two A buffers, two B buffers; the same memory stages the output tile
     constexpr int LDC = BN + 4;
-    static_assert(BM * LDC <= 2 * (BM + BN) * LDK, "output tile must fit the tile buffers");
-    __shared__ __attribute__((aligned(16))) float smem[2 * (BM + BN) * LDK];
+    constexpr int SM_TILES = 2 * (BM + BN) * LDK;
+    constexpr int SM = SM_TILES > BM * LDC ? SM_TILES : BM * LDC;
+    __shared__ __attribute__((aligned(16))) float smem[SM];
     float* const Abuf[2] = {smem, smem + BM * LDK};
     float* const Bbuf[2] = {smem + 2 * BM * LDK, smem + 2 * BM * LDK + BN * LDK};
 
@@ -73,11 +96,13 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bias_act_kernel(int M, int N
     const int wm = wave / WN;
     const int wn = wave - wm * WN;
 
-    floatx4 acc[TM][TN];
+    Acc acc[TM][TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int r = 0; r < NR; ++r) acc[i][j][r] = 0.f;
 
     // one register stage: this thread's share of an A tile and a B tile
     struct Stage {
@@ -193,28 +218,41 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bias_act_kernel(int M, int N
         }
     };
 
-    const int lrow = lane & 15;
-    const int lk = (lane >> 4) * 4;
-    const int arow0 = wm * TM * 16 + lrow;
-    const int brow0 = wn * TN * 16 + lrow;
+    // this lane's row within an MF-row block and its k offset in a 16-wide
+    // k slice (KV float4 reads of each operand per slice)
+    constexpr int KV = MF == 16 ? 1 : 2;
+    const int lrow = lane & (MF - 1);
+    const int lk = (lane / MF) * 4 * KV;
+    const int arow0 = wm * TM * MF + lrow;
+    const int brow0 = wn * TN * MF + lrow;
 
     auto multiply = [&](const float* As, const float* Bs) {
 #pragma unroll
         for (int kk = 0; kk < BK; kk += 16) {
-            floatx4 af[TM], bf[TN];
+            floatx4 af[TM][KV], bf[TN][KV];
 #pragma unroll
             for (int i = 0; i < TM; ++i)
-                af[i] = *reinterpret_cast<const floatx4*>(&As[(arow0 + i * 16) * LDK + kk + lk]);
+#pragma unroll
+                for (int v = 0; v < KV; ++v)
+                    af[i][v] = *reinterpret_cast<const floatx4*>(&As[(arow0 + i * MF) * LDK + kk + lk + 4 * v]);
 #pragma unroll
             for (int j = 0; j < TN; ++j)
-                bf[j] = *reinterpret_cast<const floatx4*>(&Bs[(brow0 + j * 16) * LDK + kk + lk]);
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
+                for (int v = 0; v < KV; ++v)
+                    bf[j][v] = *reinterpret_cast<const floatx4*>(&Bs[(brow0 + j * MF) * LDK + kk + lk + 4 * v]);
+#pragma unroll
+            for (int q = 0; q < 4 * KV; ++q)
 #pragma unroll
                 for (int i = 0; i < TM; ++i)
 #pragma unroll
-                    for (int j = 0; j < TN; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[i][q], bf[j][q], acc[i][j], 0, 0, 0);
+                    for (int j = 0; j < TN; ++j) {
+                        if constexpr (MF == 16)
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[i][0][q], bf[j][0][q], acc[i][j],
+                                                                             0, 0, 0);
+                        else
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[i][q >> 2][q & 3],
+                                                                             bf[j][q >> 2][q & 3], acc[i][j], 0, 0, 0);
+                    }
         }
     };
 
@@ -241,21 +279,23 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bias_act_kernel(int M, int N
         __syncthreads();
     }
 
-    // Accumulator layout of the 16x16 block: lane l, element r holds
-    // row 4*(l/16) + r, column l%16.  Bias and activation are applied there;
-    // the finished tile is staged in LDS (the loop above ended with a
+    // Accumulator layout of an MF x MF block: lane l holds column l % MF;
+    // element r holds row 4*(l/16) + r for MF = 16 and row
+    // 8*(r/4) + 4*(l/32) + r%4 for MF = 32.  Bias and activation are applied
+    // there; the finished tile is staged in LDS (the loop above ended with a
     // barrier) and written back row by row, 16 bytes per lane when Y allows.
     float* const Ct = smem;
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-        const int cl = wn * TN * 16 + j * 16 + (lane & 15);
+        const int cl = wn * TN * MF + j * MF + (lane & (MF - 1));
         const int n = n0 + cl;
         const float bv = (bias != nullptr && n < N) ? bias[n] : 0.f;
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int rl = wm * TM * 16 + i * 16 + (lane >> 4) * 4 + r;
+            for (int r = 0; r < NR; ++r) {
+                const int rb = MF == 16 ? (lane >> 4) * 4 + r : 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                const int rl = wm * TM * MF + i * MF + rb;
                 Ct[rl * LDC + cl] = apply_act(acc[i][j][r] + bv, act);
             }
         }
@@ -317,24 +357,25 @@ __global__ __launch_bounds__(256) void gemv_bias_act_kernel(int M, int K, const 
     if (lane == 0) y[row * ldy] = apply_act(acc + (bias ? bias[0] : 0.f), act);
 }
 
-template <int BM, int BN, int BK, int WM, int WN, bool VA, bool VB>
+template <int BM, int BN, int BK, int WM, int WN, int MF, bool VA, bool VB>
 static hipError_t launch_gemm_t(int M, int N, int K, const float* x, int64_t ld_x, const float* W,
                                 const float* bias, int act, float* y, int64_t ld_y, hipStream_t s) {
     const int tm = (M + BM - 1) / BM;
     const int tn = (N + BN - 1) / BN;
-    hipLaunchKernelGGL((gemm_bias_act_kernel<BM, BN, BK, WM, WN, VA, VB>), dim3((unsigned)(tm * tn)),
+    hipLaunchKernelGGL((gemm_bias_act_kernel<BM, BN, BK, WM, WN, MF, VA, VB>), dim3((unsigned)(tm * tn)),
                        dim3(WM * WN * 64), 0, s, M, N, K, x, ld_x, W, bias, act, y, ld_y, tm, tn,
                        (ld_y % 4 == 0) && (((uintptr_t)y & 15u) == 0));
     return hipGetLastError();
 }
 
-template <int BM, int BN, int BK, int WM, int WN>
+template <int BM, int BN, int BK, int WM, int WN, int MF>
 static hipError_t launch_gemm_v(bool va, bool vb, int M, int N, int K, const float* x, int64_t ld_x, const float* W,
                                 const float* bias, int act, float* y, int64_t ld_y, hipStream_t s) {
-    if (va && vb) return launch_gemm_t<BM, BN, BK, WM, WN, true, true>(M, N, K, x, ld_x, W, bias, act, y, ld_y, s);
-    if (va) return launch_gemm_t<BM, BN, BK, WM, WN, true, false>(M, N, K, x, ld_x, W, bias, act, y, ld_y, s);
-    if (vb) return launch_gemm_t<BM, BN, BK, WM, WN, false, true>(M, N, K, x, ld_x, W, bias, act, y, ld_y, s);
-    return launch_gemm_t<BM, BN, BK, WM, WN, false, false>(M, N, K, x, ld_x, W, bias, act, y, ld_y, s);
+    if (va && vb)
+        return launch_gemm_t<BM, BN, BK, WM, WN, MF, true, true>(M, N, K, x, ld_x, W, bias, act, y, ld_y, s);
+    if (va) return launch_gemm_t<BM, BN, BK, WM, WN, MF, true, false>(M, N, K, x, ld_x, W, bias, act, y, ld_y, s);
+    if (vb) return launch_gemm_t<BM, BN, BK, WM, WN, MF, false, true>(M, N, K, x, ld_x, W, bias, act, y, ld_y, s);
+    return launch_gemm_t<BM, BN, BK, WM, WN, MF, false, false>(M, N, K, x, ld_x, W, bias, act, y, ld_y, s);
 }
 
 static inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -355,12 +396,18 @@ hipError_t launch_linear(int64_t M, int64_t N, int64_t K, const float* x, int64_
     const bool vb = (K % 4 == 0) && aligned16(W);
     const int m = (int)M, n = (int)N, k = (int)K;
     // Tile choice measured on MI355X (inside HIP graphs) for the DLRM layer
-    // shapes: batches too small to give every CU four 64x64 tiles run best on
-    // 32x32 tiles (one 16x16 MFMA block per wave), everything else on 64x64
-    // tiles (a 32x32 sub-tile per wave).
+    // shapes:
+    //  * batches too small to give every CU four 64x64 tiles: 32x32 tiles, one
+    //    16x16 block per wave;
+    //  * K <= 16 (the first bottom layer, bound by writing y): 64x64 tiles of
+    //    32x32 blocks with 16-wide k tiles, so that no k tile is mostly padding;
+    //  * everything else (at least ~256 tiles of 128x128): 128x128 tiles, 8
+    //    waves each owning a 32x64 sub-tile of 32x32 blocks, 16-wide k tiles
+    //    (3-11% faster than 64x64 tiles of 16x16 blocks on the large layers).
     const int64_t t64 = ((M + 63) / 64) * ((N + 63) / 64);
-    if (t64 < 1024) return launch_gemm_v<32, 32, 32, 2, 2>(va, vb, m, n, k, x, ld_x, W, bias, act, y, ld_y, s);
-    return launch_gemm_v<64, 64, 32, 2, 2>(va, vb, m, n, k, x, ld_x, W, bias, act, y, ld_y, s);
+    if (t64 < 1024) return launch_gemm_v<32, 32, 32, 2, 2, 16>(va, vb, m, n, k, x, ld_x, W, bias, act, y, ld_y, s);
+    if (K <= 16) return launch_gemm_v<64, 64, 16, 2, 2, 32>(va, vb, m, n, k, x, ld_x, W, bias, act, y, ld_y, s);
+    return launch_gemm_v<128, 128, 16, 4, 2, 32>(va, vb, m, n, k, x, ld_x, W, bias, act, y, ld_y, s);
 }
 
 }  // namespace dlrm

@@ -223,6 +223,8 @@ SHAPES = [
     (2048, 512, 13), (2048, 256, 512), (2048, 64, 256), (2048, 512, 70), (2048, 512, 592),
     (2048, 1, 256), (8, 32, 4), (8, 16, 32), (8, 32, 22), (8, 1, 32),
     (33, 17, 5), (1, 1, 1), (1, 7, 3), (130, 129, 127), (1000, 300, 200), (4096, 1024, 479), (4096, 128, 256),
+    # large-batch tiles: 64x64 of 32x32 blocks for K <= 16, 128x128 otherwise (ragged M, N and K too)
+    (16384, 512, 13), (8192, 512, 512), (4100, 1030, 200),
 ]
 
 
@@ -249,6 +251,21 @@ def test_linear_no_bias_and_strided_io(orc):
     torch.cuda.synchronize()
     assert torch.all(yw[:, 96:] == 5.0)
     _linear_check(orc, x, W, None, 0, y)
+
+
+def test_linear_strided_unaligned_large_tiles(orc):
+    """Row stride 80, a start 5 floats in and K = 70: the scalar-load variants of the 128x128 tiles."""
+    gen = torch.Generator().manual_seed(3)
+    xw = torch.randn((4200, 80), generator=gen).cuda()
+    x = xw[:, 5:75]
+    W = (torch.randn((1030, 70), generator=gen) * 70 ** -0.5).cuda()
+    b = (torch.randn((1030,), generator=gen) * 70 ** -0.5).cuda()
+    yw = torch.full((4200, 1040), 5.0, device="cuda")
+    y = yw[:, :1030]
+    dl.linear_bias_act(x, W, b, dl.ACT_RELU, out=y)
+    torch.cuda.synchronize()
+    assert torch.all(yw[:, 1030:] == 5.0)
+    _linear_check(orc, x, W, b, dl.ACT_RELU, y)
 
 
 def test_linear_integer_exact():
