@@ -15,6 +15,20 @@
 
 namespace dlrm {
 
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+// Explicit LDS accesses for pointers into a dynamic LDS array: the casts make
+// sure the compiler emits ds_read / ds_write (a flat access is also counted
+// with the global loads, so every wait for it would cover those in flight).
+typedef __attribute__((address_space(3))) float lds_float;
+typedef __attribute__((address_space(3))) floatx4 lds_floatx4;
+__device__ __forceinline__ floatx4 lds_load4(const float* p) { return *(const lds_floatx4*)(const lds_float*)p; }
+__device__ __forceinline__ float lds_load(const float* p) { return *(const lds_float*)p; }
+__device__ __forceinline__ void lds_store4(float* p, floatx4 v) { *(lds_floatx4*)(lds_float*)p = v; }
+__device__ __forceinline__ void lds_store(float* p, float v) { *(lds_float*)p = v; }
+
+
 // Sum U bags per lane group.  Bag q[u] (-1 = none) is local bag number
 // q = sl * T + t of sample b_base + sl.  Lane lg of the group owns elements
 // (c * G + lg) * VEC .. + VEC-1 of the row for c < C.  Rows of one bag are
@@ -167,6 +181,72 @@ __device__ __forceinline__ void pair_dots(const float* S, int F, int D, int LDR,
                         const int j = j0 + b;
                         if (i < F && j < i) Z[s * ldz + i * (i - 1) / 2 + j] = acc[a][b];
                     }
+                }
+            }
+        }
+    }
+}
+
+// Strict-lower-triangle dots on the matrix cores, for many tables: Z[s][p] =
+// <S_s[i], S_s[j]>, p = i(i-1)/2 + j, j < i < F, with row i of sample s at
+// S + (s * F + i) * LDR in LDS and D a multiple of 16.  Wave w of the NB
+// threads takes samples w, w + NB / 64, ...  Every pair is an entry G[a][b] = <S[1 + a], S[b]>, b <= a,
+// of the product of rows 1..F-1 with rows 0..F-2, computed in 32x32 tiles
+// (J <= I; up to 32 tables one tile holds every pair) with
+// v_mfma_f32_32x32x2f32: lane l supplies A[a = l % 32][k] = row 1 + 32 I + a
+// and B[k][b = l % 32] = row 32 J + b at k = 16 c + 8 (l / 32) + q for MFMA q
+// of d-chunk c (both operands share that k order), and holds tile entry
+// (8 (r / 4) + 4 (l / 32) + r % 4, l % 32) in accumulator r.  Rows past F - 1
+// are read clamped and never stored.
+template <int NB>
+__device__ __forceinline__ void pair_dots_mfma(const float* S, int F, int D, int LDR, int nb, float* Z, int ldz) {
+    constexpr int NW = NB / 64;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int T = F - 1;
+    const int nt = (T + 31) >> 5;
+    const int r32 = lane & 31;
+    const int h = lane >> 5;
+    for (int s = wave; s < nb; s += NW) {
+        const float* Sb = S + (size_t)s * F * LDR;
+        float* Zs = Z + s * ldz;
+        for (int I = 0; I < nt; ++I) {
+            const float* ra = Sb + (1 + min(32 * I + r32, T - 1)) * LDR + 8 * h;
+            for (int J = 0; J <= I; ++J) {
+                const float* rb = Sb + min(32 * J + r32, T - 1) * LDR + 8 * h;
+                floatx16 acc;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+                // 64 values of d per group: all 16 reads first, then 32 MFMAs
+                int c = 0;
+                for (; c + 64 <= D; c += 64) {
+                    floatx4 av[8], bv[8];
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        av[2 * g] = lds_load4(ra + c + 16 * g);
+                        av[2 * g + 1] = lds_load4(ra + c + 16 * g + 4);
+                        bv[2 * g] = lds_load4(rb + c + 16 * g);
+                        bv[2 * g + 1] = lds_load4(rb + c + 16 * g + 4);
+                    }
+#pragma unroll
+                    for (int v = 0; v < 8; ++v)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av[v][q], bv[v][q], acc, 0, 0, 0);
+                }
+                for (; c < D; c += 16) {
+                    const floatx4 a0 = lds_load4(ra + c), a1 = lds_load4(ra + c + 4);
+                    const floatx4 b0 = lds_load4(rb + c), b1 = lds_load4(rb + c + 4);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a0[q], b0[q], acc, 0, 0, 0);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a1[q], b1[q], acc, 0, 0, 0);
+                }
+                const int bcol = 32 * J + r32;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int a = 32 * I + 8 * (r >> 2) + 4 * h + (r & 3);
+                    if (a < T && bcol <= a) lds_store(Zs + (a + 1) * a / 2 + bcol, acc[r]);
                 }
             }
         }

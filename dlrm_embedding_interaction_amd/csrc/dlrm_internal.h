@@ -19,6 +19,7 @@ constexpr int kRowPad = 4;                           // floats of padding per LD
 // per block (gfx950 gives a workgroup up to 160 KiB).
 constexpr int kFusedMaxLayers = 8;
 constexpr int kFusedSamples = 8;
+constexpr int kMfmaDotsMinTables = 24;           // single launch: MFMA dots for this many tables up to 32
 constexpr int kFusedThreads = 512;
 constexpr size_t kFusedMaxLds = 160 * 1024;
 

@@ -248,7 +248,10 @@ hipError_t launch_interact(const TableArgs* ta, const float* emb, int T, int D, 
     const int spb = interact_samples_per_block(T, D, B);
     // dot layout: lane-group dots for few vectors; otherwise per-lane 4x4
     // register blocks, with d split over 2 or 4 lanes while that leaves fewer
-    // work items than threads (the slices stay multiples of the vector width)
+    // work items than threads (the slices stay multiples of the vector width).
+    // (One MFMA tile per sample, as the single launch uses, measured slower
+    // here: 4 waves carry up to 16 samples, and a tile computes the whole
+    // square.)
     const int F = T + 1;
     const int n4 = (F - 1 + 3) / 4;
     const int items = spb * n4 * (n4 + 1) / 2;

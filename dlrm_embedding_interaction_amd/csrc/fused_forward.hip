@@ -32,19 +32,6 @@
 
 namespace dlrm {
 
-typedef float floatx4 __attribute__((ext_vector_type(4)));
-
-// Explicit LDS accesses: the activation buffers are reached through pointer
-// arithmetic on the dynamic LDS array, and the casts make sure the compiler
-// emits ds_read / ds_write (a flat access would be counted with the global
-// weight loads and make every wait cover the whole prefetch ring).
-typedef __attribute__((address_space(3))) float lds_float;
-typedef __attribute__((address_space(3))) floatx4 lds_floatx4;
-__device__ __forceinline__ floatx4 lds_load4(const float* p) { return *(const lds_floatx4*)(const lds_float*)p; }
-__device__ __forceinline__ float lds_load(const float* p) { return *(const lds_float*)p; }
-__device__ __forceinline__ void lds_store4(float* p, floatx4 v) { *(lds_floatx4*)(lds_float*)p = v; }
-__device__ __forceinline__ void lds_store(float* p, float v) { *(lds_float*)p = v; }
-
 // Raw buffer loads of the packed weights: a load whose offset lies past the
 // buffer's size returns zeros without a memory access, so a step past a
 // layer's last chunk still issues its loads (every wait keeps counting
@@ -368,7 +355,10 @@ __global__ __launch_bounds__(kFusedThreads) void fused_forward_kernel(FusedArgs 
     __syncthreads();
 
     // 5. strict-lower-triangle dots into R[:, D:D+P]
-    pair_dots<4, G, 1, RT, NT>(feat, F, D, LDR, nb, Rb + D, lda, fa.dsplit);
+    if constexpr (RT == 32)
+        pair_dots_mfma<NT>(feat, F, D, LDR, nb, Rb + D, lda);
+    else
+        pair_dots<4, G, 1, RT, NT>(feat, F, D, LDR, nb, Rb + D, lda, fa.dsplit);
     zero_columns<S>(Rb, lda, D + F * (F - 1) / 2, (D + F * (F - 1) / 2 + 63) & ~63);
     __syncthreads();
     cur ^= 1;
@@ -473,11 +463,19 @@ static hipError_t launch_fused_s(FusedArgs& fa, bool multi_hot, hipStream_t s) {
     while (dsplit < 4 && items * dsplit * 2 <= kFusedThreads && fa.D % (4 * dsplit * 2) == 0) dsplit *= 2;
     fa.dsplit = dsplit;
     const int g = pow2_at_least((fa.D + 3) / 4);
+    // dots: flat pairs for few tables, 4x4 register blocks, or one 32x32
+    // MFMA tile per sample for kMfmaDotsMinTables..32 tables (D a multiple
+    // of 16; measured faster there, slower with fewer tables or more tiles)
+    const bool mfma_dots = fa.T >= kMfmaDotsMinTables && fa.T <= 32 && fa.D % 16 == 0;
 #define FUSED_G(G_)                                                                                 \
     case G_:                                                                                        \
         if (F <= 12) {                                                                              \
             if (multi_hot) return launch_fused_t<S, G_, 4, 4, 0>(fa, s);                            \
             return launch_fused_t<S, G_, 8, 1, 0>(fa, s);                                           \
+        }                                                                                           \
+        if (mfma_dots) {                                                                            \
+            if (multi_hot) return launch_fused_t<S, G_, 4, 4, 32>(fa, s);                           \
+            return launch_fused_t<S, G_, 8, 1, 32>(fa, s);                                          \
         }                                                                                           \
         if (multi_hot) return launch_fused_t<S, G_, 4, 4, 4>(fa, s);                                \
         return launch_fused_t<S, G_, 8, 1, 4>(fa, s);

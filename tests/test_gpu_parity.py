@@ -337,7 +337,10 @@ def test_forward_layerwise_through_standalone_calls(orc):
 
 @pytest.mark.parametrize("path", ["fused", "layered"])
 @pytest.mark.parametrize("B,T", [(16, 1), (16, 32), (64, 8), (256, 4), (2048, 16), (4096, 1), (16384, 8),
-                                 (16384, 32)])
+                                 (16384, 32),
+                                 # the single launch's dots: one MFMA tile per sample from 24 to 32 tables,
+                                 # 4x4 register blocks beyond (sweep shapes with other table counts)
+                                 (256, 24), (2048, 24), (3000, 32), (64, 40)])
 def test_forward_sweep_cells(B, T, path, orc):
     log(f"sweep cell b={B} t={T} ({path})")
     w = di.sweep(B, T)
@@ -475,7 +478,8 @@ def test_forward_graph_capture_replays_match_eager(path):
 # --- fused bag gather + interaction ---------------------------------------------
 
 
-@pytest.mark.parametrize("T,D,L", [(3, 16, 1), (3, 64, 1), (32, 64, 1), (26, 128, 20), (5, 6, 3), (8, 512, 2)])
+@pytest.mark.parametrize("T,D,L", [(3, 16, 1), (3, 64, 1), (32, 64, 1), (26, 128, 20), (5, 6, 3), (8, 512, 2),
+                                   (28, 48, 1), (24, 80, 3), (33, 64, 1)])
 def test_embbag_interact_integer_bitexact(T, D, L, orc):
     w = di.custom(f"fused_{T}_{D}_{L}", 150, 3, T, 400, D, L, (3, D), cfg_id=15)
     inp = di.make_inputs(w, int_tables=True)
@@ -603,6 +607,17 @@ def test_stacked_table_layout_is_bit_identical():
         fa = dl.Model.from_inputs(inp).forward(inp.dense, inp.indices, inp.offsets, path=path).clone()
         fb = dl.Model.from_inputs(sv).forward(inp.dense, inp.indices, inp.offsets, path=path)
         assert torch.equal(fa, fb)
+
+
+@pytest.mark.parametrize("T,D,L", [(26, 128, 20), (28, 48, 1), (24, 80, 2), (32, 16, 1), (23, 64, 1)])
+def test_forward_fused_gram_dots(T, D, L, orc):
+    """Single launch with 24-32 tables: the dots as one 32x32 MFMA tile per sample, over d in
+    groups of 64 and a 16-wide tail (D = 48, 80, 16), with multi-hot bags; 23 tables stay on
+    the register-block dots."""
+    w = di.custom(f"gram_{T}_{D}_{L}", 300, 13, T, 2000, D, L, (13, 64, D), hidden_top=(128,),
+                  dist="zipf" if L > 1 else "uniform", cfg_id=25)
+    inp = di.make_inputs(w)
+    _forward_check(inp, on_gpu(inp), orc, path="fused")
 
 
 @pytest.mark.parametrize("T,D", [(64, 64), (2, 1024), (40, 33)])
