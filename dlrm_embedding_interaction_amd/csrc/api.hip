@@ -319,7 +319,7 @@ bool fused_preferred(const dlrm_model_t* m, int64_t batch) {
     if (m->num_tables >= 24) {
         // one MFMA tile per sample takes the dots up to 32 tables (D % 16 == 0)
         const bool gram = m->num_tables <= 32 && m->emb_dim % 16 == 0;
-        return batch >= 1024 && batch <= (gram ? 4096 : 2048);
+        return gram ? batch >= 512 && batch <= 4096 : batch >= 1024 && batch <= 2048;
     }
     if (m->num_tables >= 12) return batch >= 512;
     return true;
