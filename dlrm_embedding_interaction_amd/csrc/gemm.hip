@@ -40,6 +40,16 @@ __device__ __forceinline__ float apply_act(float v, int act) {
     return v;
 }
 
+// Four consecutive floats from global memory at a 4-byte-aligned address.
+// gfx9 vector-memory loads of 16 bytes need only dword alignment, so this is
+// one dwordx4 load also where a row starts off a 16-byte boundary (a Linear
+// weight (N, K) with K not a multiple of 4, or x with such a row stride).
+__device__ __forceinline__ floatx4 load4_dword_aligned(const float* p) {
+    floatx4 v;
+    __builtin_memcpy(&v, p, sizeof(v));
+    return v;
+}
+
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 template <int MF>
@@ -129,7 +139,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bias_act_kernel(int M, int N
                 if (m < M) {
                     const float* p = A + (int64_t)m * lda + k;
                     if (k + 3 < K) {
-                        v = *reinterpret_cast<const floatx4*>(p);
+                        v = load4_dword_aligned(p);
                     } else {
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
@@ -159,7 +169,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bias_act_kernel(int M, int N
                 if (n < N) {
                     const float* p = W + (int64_t)n * K + k;
                     if (k + 3 < K) {
-                        v = *reinterpret_cast<const floatx4*>(p);
+                        v = load4_dword_aligned(p);
                     } else {
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
@@ -379,6 +389,7 @@ static hipError_t launch_gemm_v(bool va, bool vb, int M, int N, int K, const flo
 }
 
 static inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+static inline bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
 
 hipError_t launch_linear(int64_t M, int64_t N, int64_t K, const float* x, int64_t ld_x, const float* W,
                          const float* bias, int act, float* y, int64_t ld_y, hipStream_t s) {
@@ -393,7 +404,9 @@ hipError_t launch_linear(int64_t M, int64_t N, int64_t K, const float* x, int64_
                                x, ld_x, W, bias, act, y, ld_y);
         return hipGetLastError();
     }
-    const bool vb = (K % 4 == 0) && aligned16(W);
+    // GEMM tiles take float4 loads of x and W from any 4-byte-aligned rows
+    const bool vb = aligned4(W);
+    const bool vx = aligned4(x);
     const int m = (int)M, n = (int)N, k = (int)K;
     // Tile choice measured on MI355X (inside HIP graphs) for the DLRM layer
     // shapes:
@@ -405,9 +418,9 @@ hipError_t launch_linear(int64_t M, int64_t N, int64_t K, const float* x, int64_
     //    waves each owning a 32x64 sub-tile of 32x32 blocks, 16-wide k tiles
     //    (3-11% faster than 64x64 tiles of 16x16 blocks on the large layers).
     const int64_t t64 = ((M + 63) / 64) * ((N + 63) / 64);
-    if (t64 < 1024) return launch_gemm_v<32, 32, 32, 2, 2, 16>(va, vb, m, n, k, x, ld_x, W, bias, act, y, ld_y, s);
-    if (K <= 16) return launch_gemm_v<64, 64, 16, 2, 2, 32>(va, vb, m, n, k, x, ld_x, W, bias, act, y, ld_y, s);
-    return launch_gemm_v<128, 128, 16, 4, 2, 32>(va, vb, m, n, k, x, ld_x, W, bias, act, y, ld_y, s);
+    if (t64 < 1024) return launch_gemm_v<32, 32, 32, 2, 2, 16>(vx, vb, m, n, k, x, ld_x, W, bias, act, y, ld_y, s);
+    if (K <= 16) return launch_gemm_v<64, 64, 16, 2, 2, 32>(vx, vb, m, n, k, x, ld_x, W, bias, act, y, ld_y, s);
+    return launch_gemm_v<128, 128, 16, 4, 2, 32>(vx, vb, m, n, k, x, ld_x, W, bias, act, y, ld_y, s);
 }
 
 }  // namespace dlrm
