@@ -207,9 +207,11 @@ __device__ __forceinline__ void mlp_layer(const float* in, int ldi, int K, const
 }
 
 // Layer dispatch: TW = tiles per wave and pass, KU chunks of 16 k per step and
-// PD steps in flight, so that each of the 8 waves keeps 24 weight loads (24
-// KiB) outstanding -- the L2 stream into one CU is latency-bound, so the
-// more requests in flight the higher its rate.
+// PD steps in flight.  Layers of one or two tiles per wave keep 2 steps (8
+// weight loads, 8 KiB per wave) in flight: measured on MI355X, deeper rings
+// there leave the waves stalled on the CU's vector-memory queue, which holds
+// up their MFMAs too (512->256 layer 6.9 -> 6.3 us, 256->64 2.6 -> 2.1 us at
+// 8 samples); four-tile layers keep 6 steps.
 template <int S>
 __device__ __forceinline__ void mlp_layer_any(const float* in, int ldi, int K, const float* Wp, const float* bias,
                                               int N, bool relu, float* out, int ldo) {
@@ -224,15 +226,19 @@ __device__ __forceinline__ void mlp_layer_any(const float* in, int ldi, int K, c
     const int nkc = (K + 15) >> 4;
     // short rings for the short layers, so that few steps are padding
     if (tw <= 1) {
-        if (nkc <= 16) DLRM_LAYER(1, 4, 4)
-        DLRM_LAYER(1, 4, 6)
+        if constexpr (S > 8) {
+            if (nkc <= 16) DLRM_LAYER(1, 4, 4)
+            DLRM_LAYER(1, 4, 6)
+        } else {
+            DLRM_LAYER(1, 4, 2)
+        }
     }
     if constexpr (S > 8) {
         // 16 samples: two tiles per wave and pass at most (registers)
         if (nkc <= 1) DLRM_LAYER(2, 1, 1)
         DLRM_LAYER(2, 2, 6)
     } else {
-        if (tw <= 2) DLRM_LAYER(2, 2, 6)
+        if (tw <= 2) DLRM_LAYER(2, 2, 2)
         if (nkc <= 1) DLRM_LAYER(4, 1, 1)
         DLRM_LAYER(4, 1, 6)
     }
