@@ -309,9 +309,10 @@ bool model_fits_fused(const dlrm_model_t* m) {
 // across the whole chip.  Measured on MI355X over the batch x tables sweep
 // of the 13-512-256-64 / (64+P)-512-256-1 model (both paths replayed from
 // graphs of 8 steps): the single launch is faster up to batch 8192 with up
-// to 8 tables, from batch 512 with 16 tables, and only from 1024 to 2048 with
-// 32 tables, where gathering 32 bags and streaming the 592-wide first top
-// layer per block dominate.
+// to 16 tables; with 32 tables only from 512 to 4096 when the dots run as one
+// MFMA tile per sample (else from 1024 to 2048), since below that gathering
+// 32 bags and streaming the 592-wide first top layer per block cost more
+// than the layered path's launches.
 constexpr int64_t kFusedAutoMaxBatch = 8192;
 constexpr int64_t kFusedAutoMaxWeightBytes = 3 << 20;
 bool fused_preferred(const dlrm_model_t* m, int64_t batch) {
@@ -321,7 +322,6 @@ bool fused_preferred(const dlrm_model_t* m, int64_t batch) {
         const bool gram = m->num_tables <= 32 && m->emb_dim % 16 == 0;
         return gram ? batch >= 512 && batch <= 4096 : batch >= 1024 && batch <= 2048;
     }
-    if (m->num_tables >= 12) return batch >= 512;
     return true;
 }
 
