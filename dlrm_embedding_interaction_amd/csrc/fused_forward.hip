@@ -210,8 +210,9 @@ __device__ __forceinline__ void mlp_layer(const float* in, int ldi, int K, const
 // PD steps in flight.  Layers of one or two tiles per wave keep 2 steps (8
 // weight loads, 8 KiB per wave) in flight: measured on MI355X, deeper rings
 // there leave the waves stalled on the CU's vector-memory queue, which holds
-// up their MFMAs too (512->256 layer 6.9 -> 6.3 us, 256->64 2.6 -> 2.1 us at
-// 8 samples); four-tile layers keep 6 steps.
+// up their MFMAs too (8 samples: 512->256 layer 6.9 -> 6.3 us, 256->64 2.6 ->
+// 2.1 us; 16 samples: batch 4096 x 4 tables 44.3 -> 42.5 us per forward);
+// four-tile layers keep 6 steps.
 template <int S>
 __device__ __forceinline__ void mlp_layer_any(const float* in, int ldi, int K, const float* Wp, const float* bias,
                                               int N, bool relu, float* out, int ldo) {
@@ -226,17 +227,12 @@ __device__ __forceinline__ void mlp_layer_any(const float* in, int ldi, int K, c
     const int nkc = (K + 15) >> 4;
     // short rings for the short layers, so that few steps are padding
     if (tw <= 1) {
-        if constexpr (S > 8) {
-            if (nkc <= 16) DLRM_LAYER(1, 4, 4)
-            DLRM_LAYER(1, 4, 6)
-        } else {
-            DLRM_LAYER(1, 4, 2)
-        }
+        DLRM_LAYER(1, 4, 2)
     }
     if constexpr (S > 8) {
         // 16 samples: two tiles per wave and pass at most (registers)
         if (nkc <= 1) DLRM_LAYER(2, 1, 1)
-        DLRM_LAYER(2, 2, 6)
+        DLRM_LAYER(2, 2, 2)
     } else {
         if (tw <= 2) DLRM_LAYER(2, 2, 2)
         if (nkc <= 1) DLRM_LAYER(4, 1, 1)
