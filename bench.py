@@ -107,8 +107,8 @@ def algorithmic(w):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py: this build measures one GPU only; --gpus must be 1 "
-              "(the forward shards by batch with no exchange, see the design notes)", file=sys.stderr)
+        print("bench.py measures one GPU only; --gpus must be 1 (the forward shards by batch, with no "
+              "exchange between GPUs, so one GPU's share at its real batch is what it times)", file=sys.stderr)
         sys.exit(2)
 
     import torch
