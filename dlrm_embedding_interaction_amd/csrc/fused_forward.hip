@@ -127,8 +127,11 @@ __device__ __forceinline__ void mlp_layer(const float* in, int ldi, int K, const
             const int t = t0 + wave + NW * u;
             wtile[u] = t < ntile ? ((uint32_t)t * nkc * 64u + lane) * 16u : kOutOfRange;
             const int n0 = 16 * t + 4 * fg;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) bv[u][r] = lds_load(bias + min(n0 + r, N - 1));  // staged in LDS
+            // the 4 biases of this lane's features in one LDS read: each bias
+            // segment of the staged tail starts 16-byte aligned and is zero-
+            // padded to a multiple of 4; lanes past N read any aligned group
+            // (their outputs are never kept)
+            bv[u] = lds_load4(bias + (n0 < N ? n0 : 0));
 #pragma unroll
             for (int sg = 0; sg < SG; ++sg) acc[u][sg] = floatx4{0.f, 0.f, 0.f, 0.f};
         }
