@@ -18,7 +18,7 @@
 //    l = 16 fg + 4 kg + e supplies W[f = 4 fg + e][k = 4 kg + q] as A and
 //    act[sample e][k] as B, so one instruction covers 16 features x 4 samples
 //    x 4 k values at the full fp32 MFMA rate even with 4-sample groups; the
-//    4 k groups are added afterwards with two DPP row shifts;
+//    4 k groups are added afterwards with two DPP row rotations;
 //  * the bags are gathered with the same lane-group code as the standalone
 //    bag kernel and the dots reuse the interaction kernel's LDS routine;
 //  * nothing leaves the block but the S sigmoid outputs.
@@ -46,11 +46,12 @@ __device__ __forceinline__ floatx4 buffer_load4(__amdgpu_buffer_rsrc_t r, uint32
     return __builtin_bit_cast(floatx4, v);
 }
 
-__device__ __forceinline__ float dpp_row_shr4(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x114, 0xF, 0xF, false));
+// Rotations by 4 and 8 lanes within each 16-lane row.
+__device__ __forceinline__ float dpp_row_ror4(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, false));
 }
-__device__ __forceinline__ float dpp_row_shr8(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x118, 0xF, 0xF, false));
+__device__ __forceinline__ float dpp_row_ror8(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));
 }
 
 // out[s][c] = 0 for s < S and c in [c0, c1) (all threads of the block).
@@ -120,18 +121,15 @@ __device__ __forceinline__ void mlp_layer(const float* in, int ldi, int K, const
         if (t0 + wave >= ntile) break;
         uint32_t wtile[TW];  // byte offset of this lane's first chunk of each tile
         floatx4 acc[TW][SG];
-        floatx4 bv[TW];
+        float bv[TW];
 #pragma unroll
         for (int u = 0; u < TW; ++u) {
             // tiles past the last read zeros and are never stored
             const int t = t0 + wave + NW * u;
             wtile[u] = t < ntile ? ((uint32_t)t * nkc * 64u + lane) * 16u : kOutOfRange;
-            const int n0 = 16 * t + 4 * fg;
-            // the 4 biases of this lane's features in one LDS read: each bias
-            // segment of the staged tail starts 16-byte aligned and is zero-
-            // padded to a multiple of 4; lanes past N read any aligned group
-            // (their outputs are never kept)
-            bv[u] = lds_load4(bias + (n0 < N ? n0 : 0));
+            // the bias of the one output this lane finishes (feature 16 t + 4 fg + kg)
+            const int n = 16 * t + 4 * fg + kg;
+            bv[u] = lds_load(bias + (n < N ? n : 0));
 #pragma unroll
             for (int sg = 0; sg < SG; ++sg) acc[u][sg] = floatx4{0.f, 0.f, 0.f, 0.f};
         }
@@ -184,30 +182,30 @@ __device__ __forceinline__ void mlp_layer(const float* in, int ldi, int K, const
         for (int p = 0; p < PD; ++p)
             if (p < rest) step(trips * PD + p, ring[p]);
         // VGPR r of lane 16 fg + 4 kg + e holds the partial sum over the k
-        // group kg for feature 16 t + 4 fg + r and sample 4 sg + e; two row
-        // shifts leave the total over kg in the lanes with kg = 3.
+        // group kg for feature 16 t + 4 fg + r and sample 4 sg + e.  Two row
+        // rotations (by 4, then 8 lanes) leave the total over kg in all four
+        // lanes of a group; lane kg then finishes feature 16 t + 4 fg + kg,
+        // so that every lane does one output's bias, activation and store.
 #pragma unroll
         for (int u = 0; u < TW; ++u) {
             const int t = t0 + wave + NW * u;
             if (t >= ntile) break;
-            const int n0 = 16 * t + 4 * fg;
+            const int n = 16 * t + 4 * fg + kg;
 #pragma unroll
             for (int sg = 0; sg < SG; ++sg) {
                 floatx4 v = acc[u][sg];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    v[r] += dpp_row_shr4(v[r]);
-                    v[r] += dpp_row_shr8(v[r]);
+                    v[r] += dpp_row_ror4(v[r]);
+                    v[r] += dpp_row_ror8(v[r]);
                 }
-                if (kg == 3) {
-                    floatx4 o;
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const float y = v[r] + bv[u][r];
-                        o[r] = (n0 + r < N) ? (relu ? fmaxf(y, 0.f) : y) : 0.f;
-                    }
-                    lds_store4(out + (4 * sg + e) * ldo + n0, o);
-                }
+                // v[kg], as two levels of selects (no branches)
+                const float lo = (kg & 1) ? v[1] : v[0];
+                const float hi = (kg & 1) ? v[3] : v[2];
+                float y = (kg & 2) ? hi : lo;
+                y += bv[u];
+                y = relu ? fmaxf(y, 0.f) : y;
+                lds_store(out + (4 * sg + e) * ldo + n, n < N ? y : 0.f);
             }
         }
     }
