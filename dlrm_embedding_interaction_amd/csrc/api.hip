@@ -309,7 +309,7 @@ bool model_fits_fused(const dlrm_model_t* m) {
 // across the whole chip.  Measured on MI355X over the batch x tables sweep
 // of the 13-512-256-64 / (64+P)-512-256-1 model (both paths replayed from
 // graphs of 8 steps): the single launch is faster up to batch 8192 with up
-// to 16 tables; with 32 tables only from 512 to 4096 when the dots run as one
+// to 16 tables; with 32 tables only from 256 to 4096 when the dots run as one
 // MFMA tile per sample (else from 1024 to 2048), since below that gathering
 // 32 bags and streaming the 592-wide first top layer per block cost more
 // than the layered path's launches.
@@ -320,7 +320,7 @@ bool fused_preferred(const dlrm_model_t* m, int64_t batch) {
     if (m->num_tables >= 24) {
         // one MFMA tile per sample takes the dots up to 32 tables (D % 16 == 0)
         const bool gram = m->num_tables <= 32 && m->emb_dim % 16 == 0;
-        return gram ? batch >= 512 && batch <= 4096 : batch >= 1024 && batch <= 2048;
+        return gram ? batch >= 256 && batch <= 4096 : batch >= 1024 && batch <= 2048;
     }
     return true;
 }

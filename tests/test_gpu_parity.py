@@ -419,7 +419,7 @@ def test_forward_auto_path_choice():
         unpacked.forward(g.dense, g.indices, g.offsets, path="fused")
     assert e.value.code == dl.DLRM_E_NULL
     cases = [di.custom("big_top", 96, 13, 3, 1000, 64, 1, (13, 64), hidden_top=(1024, 1024), cfg_id=23),
-             di.sweep(16384, 1), di.sweep(256, 32)]
+             di.sweep(16384, 1), di.sweep(128, 32)]
     for w in cases:
         g = on_gpu(di.make_inputs(w))
         m = dl.Model.from_inputs(g)
