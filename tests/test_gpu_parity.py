@@ -394,6 +394,18 @@ def test_forward_odd_layer_shapes(ln_bot, hidden_top, D, path, orc):
     _forward_check(inp, on_gpu(inp), orc, path=path)
 
 
+@pytest.mark.parametrize("ln_bot,hidden_top,D", [((13, 37, 16), (), 16), ((3, 300, 100, 48), (129, 17), 48),
+                                                 ((13, 24, 20, 28, 32, 36, 40, 44, 52), (8,) * 7, 52)])
+def test_forward_odd_layer_shapes_sixteen_samples_per_block(ln_bot, hidden_top, D, orc):
+    """The same odd widths past batch 2048, where the single launch carries 16
+    samples per block (2-step weight rings, partly filled last tiles, waves
+    without a tile), and a ragged last block."""
+    w = di.custom(f"odd16_{len(ln_bot)}_{D}", 2100, ln_bot[0], 5, 900, D, 2, ln_bot, hidden_top=hidden_top,
+                  cfg_id=25)
+    inp = di.make_inputs(w)
+    _forward_check(inp, on_gpu(inp), orc, path="fused")
+
+
 @pytest.mark.parametrize("path", ["fused", "layered"])
 def test_forward_zero_last_layer_gives_exactly_half(path):
     inp = di.make_inputs(di.PAGE4)
