@@ -363,10 +363,31 @@ __global__ __launch_bounds__(kFusedThreads) void fused_forward_kernel(FusedArgs 
     __syncthreads();
 
     // 5. strict-lower-triangle dots into R[:, D:D+P]
-    if constexpr (RT == 32)
+    if constexpr (RT == 32) {
         pair_dots_mfma<NT>(feat, F, D, LDR, nb, Rb + D, lda);
-    else
+    } else if (RT == 0 && nb * (F * (F - 1) / 2) <= NT) {
+        // few pairs (few tables): one thread per pair dot, no lane-group sums
+        const int P = F * (F - 1) / 2;
+        if (tid < nb * P) {
+            const int s = tid / P;
+            const int p = tid - s * P;
+            int i, j;
+            pair_from_flat(p, i, j);
+            const float* si = feat + ((size_t)s * F + i) * LDR;
+            const float* sj = feat + ((size_t)s * F + j) * LDR;
+            float acc = 0.f;
+            for (int d = 0; d < D; d += 4) {
+                const floatx4 a = lds_load4(si + d), b = lds_load4(sj + d);
+                acc = fmaf(a[0], b[0], acc);
+                acc = fmaf(a[1], b[1], acc);
+                acc = fmaf(a[2], b[2], acc);
+                acc = fmaf(a[3], b[3], acc);
+            }
+            lds_store(Rb + s * lda + D + p, acc);
+        }
+    } else {
         pair_dots<4, G, 1, RT, NT>(feat, F, D, LDR, nb, Rb + D, lda, fa.dsplit);
+    }
     zero_columns<S>(Rb, lda, D + F * (F - 1) / 2, (D + F * (F - 1) / 2 + 63) & ~63);
     __syncthreads();
     cur ^= 1;
