@@ -7,10 +7,13 @@ that consecutive steps gather different rows.  By default the steps are
 replayed from HIP graphs (captured once, outside the timed region) so that
 host launch overhead does not hide the kernels: the timed run replays graphs
 of --graph-steps consecutive steps (one graph launch per 8 forwards, as a
-serving loop would), the percentiles and the cold-cache figure time single
-steps, and --eager times plain calls.
+serving loop would; when --steps is not a multiple of it, one more graph holds
+the remaining steps, so every timed step is a replay of the same form), the
+percentiles and the cold-cache figure time single-step replays, and --eager
+times plain calls.
 
-Printed: one JSON line with the contract fields, plus
+Printed: one JSON line with the contract fields (the page-4 workload: batch
+2048, 3 tables), plus
   path              the path dlrm_forward takes for the workload: "fused"
                     (the whole forward in one kernel) or "layered";
   roofline          the dominant kernel of that path against its roofline,
@@ -20,9 +23,15 @@ Printed: one JSON line with the contract fields, plus
   roofline_emb_interact  the bag-gather + interaction kernel (dlrm_embbag_interact);
   kernels           per-kernel average durations (HIP events): the
                     single-launch forward and each stage of the layered path;
-  cpu_baseline      the fp64 oracle timed on the host cores on a bounded
-                    sample of the workload;
-  secondary         the 32-table workload (bs 2048) when --secondary is given.
+  nc32              the same figures for the 32-table workload (batch 2048),
+                    the metric's second configuration;
+  ceilings          the library's own HBM read-stream and random-row gather
+                    rates (dlrm_probe_read_stream / dlrm_probe_gather_rows);
+  emb_interact_large  dlrm_embbag_interact at batch 16384 with 8, 16 and 32
+                    tables: us, algorithmic GB/s and fractions of 8 TB/s and
+                    of the ceilings;
+  cpu_baseline      the fp64 oracle on the host: the full page-4 and 32-table
+                    batches on one thread and on all the cores it may use.
 """
 from __future__ import annotations
 
@@ -55,8 +64,12 @@ def parse():
     p.add_argument("--path", default="auto", choices=["auto", "fused", "layered"],
                    help="dlrm_forward (auto), dlrm_forward_fused or dlrm_forward_layered")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-seconds", type=float, default=10.0)
-    p.add_argument("--secondary", action="store_true", help="also time the 32-table workload")
+    p.add_argument("--cpu-seconds", type=float, default=2.0,
+                   help="least time per CPU-baseline measurement (whole forwards are repeated until it passes)")
+    p.add_argument("--no-secondary", action="store_true", help="skip the 32-table workload")
+    p.add_argument("--no-large", action="store_true", help="skip the batch-16384 bag + interaction cells")
+    p.add_argument("--index-bytes", type=int, default=8, choices=[4, 8],
+                   help="width of the indices and offsets handed to the library")
     p.add_argument("--kernel-reps", type=int, default=50)
     p.add_argument("--cold-steps", type=int, default=20,
                    help="forwards timed one by one after a 1 GiB flush of the caches (0: skip)")
@@ -67,10 +80,10 @@ def parse():
     return p.parse_args()
 
 
-def fused_algorithmic(w):
+def fused_algorithmic(w, ib=8):
     """Algorithmic flops and HBM bytes of one single-launch forward: every
-    Linear layer and the dots; dense rows, gathered rows, indices, offsets,
-    the weights once and the outputs."""
+    Linear layer and the dots; dense rows, gathered rows, indices and offsets
+    (ib bytes each), the weights once and the outputs."""
     B, T, D, L = w.batch, w.num_tables, w.dim, w.bag
     flops = 2 * B * w.n_pairs * D
     wbytes = 0
@@ -78,13 +91,13 @@ def fused_algorithmic(w):
         for K, N in zip(ln[:-1], ln[1:]):
             flops += 2 * B * N * K
             wbytes += 4 * (N * K + N)
-    nbytes = 4 * B * w.ln_bot[0] + B * T * L * (D * 4 + 8) + B * T * 8 + wbytes + 4 * B
+    nbytes = 4 * B * w.ln_bot[0] + B * T * L * (D * 4 + ib) + B * T * ib + wbytes + 4 * B
     return dict(name="fused_forward", kind="mfma", flops=flops, bytes=nbytes, M=B)
 
 
-def algorithmic(w):
+def algorithmic(w, ib=8):
     """Algorithmic bytes / flops per launch of each stage of the layered path
-    (what the method must move or compute)."""
+    (what the method must move or compute; indices and offsets of ib bytes)."""
     B, T, D, L = w.batch, w.num_tables, w.dim, w.bag
     P = w.n_pairs
     stages = []
@@ -94,7 +107,7 @@ def algorithmic(w):
         stages.append(dict(name=f"bot{l}", kind="mfma" if N > 1 else "hbm", flops=2 * B * N * K,
                            bytes=4 * (B * K + N * K + N + B * N), M=B, N=N, K=K))
     # fused gather + interaction: rows, indices, offsets, x read, Z written
-    emb_bytes = B * T * L * (D * 4 + 8) + B * T * 8 + B * D * 4 + B * P * 4
+    emb_bytes = B * T * L * (D * 4 + ib) + B * T * ib + B * D * 4 + B * P * 4
     stages.append(dict(name="emb_interact", kind="hbm", flops=2 * B * P * D, bytes=emb_bytes))
     ln = list(w.ln_top)
     for l in range(len(ln) - 1):
@@ -129,6 +142,7 @@ def main():
 
     res = run_workload(torch, dl, di, w, dev, args)
     lay = res["layered"]
+    G = 1 if args.eager else max(1, min(args.graph_steps, args.steps))
     out = {
         "metric": "DLRMv1 fwd µs @bs2048 nc=3/32; samples/s; emb-bag+interact HBM GB/s",
         "value": res["samples_per_s"],
@@ -146,8 +160,8 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "num_tables": w.num_tables, "rows_per_table": w.rows,
                    "dim": w.dim, "bag": w.bag, "ln_bot": list(w.ln_bot), "ln_top": list(w.ln_top),
                    "mode": "eager" if args.eager else "hip_graph", "index_sets": args.index_sets,
-                   "steps_per_graph": 1 if args.eager else max(1, min(args.graph_steps, args.steps)),
-                   "path": res["path"]},
+                   "steps_per_graph": G, "remainder_graph_steps": 0 if args.eager else args.steps % G,
+                   "index_bytes": args.index_bytes, "path": res["path"]},
         "path": res["path"],
         "us_per_forward_p10_p50_p90": [res["pct"]["p10"], res["pct"]["p50"], res["pct"]["p90"]],
         "us_per_forward_cold_p50": res["cold_us"],
@@ -159,23 +173,27 @@ def main():
         "mlp_frac_of_fp32_mfma_peak": res["mlp_tflops"] / FP32_MFMA_PEAK_TFLOPS,
         "kernels": res["kernels"],
     }
+    ceil = None
     if not args.copy_calibration:   # counter runs keep the calibration copy the only copy kernel
-        ceiling = copy_ceiling(torch, dev)
-        out["copy_ceiling_GBps"] = ceiling
-        out["roofline_emb_interact"]["frac_of_copy_ceiling"] = out["roofline_emb_interact"]["achieved"] / ceiling
-    if args.secondary:
+        ceil = ceilings(torch, dl, dev)
+        out["ceilings"] = ceil
+        re = out["roofline_emb_interact"]
+        re["frac_of_read_ceiling"] = re["achieved"] / ceil["read_stream_GBps"]
+    if not args.no_secondary and w.name != di.MANYTABLE.name:
         w2 = di.MANYTABLE
         r2 = run_workload(torch, dl, di, w2, dev, args)
-        out["secondary"] = {w2.name: {"path": r2["path"], "us_per_forward": r2["ms_per_step"] * 1e3,
-                                      "us_per_forward_p10_p50_p90": [r2["pct"]["p10"], r2["pct"]["p50"],
-                                                                     r2["pct"]["p90"]],
-                                      "us_per_forward_cold_p50": r2["cold_us"],
-                                      "mlp_TFLOPs": r2["mlp_tflops"],
-                                      "samples_per_s": r2["samples_per_s"],
-                                      "emb_interact_GBps": r2["roofline_emb"]["achieved"],
-                                      "roofline": r2["roofline"], "roofline_emb_interact": r2["roofline_emb"]}}
+        out["nc32"] = {"workload": w2.name, "batch": w2.batch, "num_tables": w2.num_tables, "path": r2["path"],
+                       "us_per_forward": r2["ms_per_step"] * 1e3, "samples_per_s": r2["samples_per_s"],
+                       "us_per_forward_p10_p50_p90": [r2["pct"]["p10"], r2["pct"]["p50"], r2["pct"]["p90"]],
+                       "us_per_forward_cold_p50": r2["cold_us"],
+                       "mlp_TFLOPs": r2["mlp_tflops"],
+                       "emb_interact_GBps": r2["roofline_emb"]["achieved"],
+                       "roofline": r2["roofline"], "roofline_emb_interact": r2["roofline_emb"]}
+    if not args.no_large:
+        out["emb_interact_large"] = large_cells(torch, dl, di, dev, args, ceil)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        extra = [] if args.no_secondary or w.name == di.MANYTABLE.name else [di.MANYTABLE]
+        out["cpu_baseline"] = cpu_baseline([w] + extra, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 
@@ -190,6 +208,9 @@ def run_workload(torch, dl, di, w, dev, args):
     idx_sets = [inp.indices]
     for s in range(1, nsets):
         idx_sets.append(di.make_indices(w, device=dev, seed=di.BASE_SEED + 7919 * s))
+    itype = torch.int32 if args.index_bytes == 4 else torch.int64
+    idx_sets = [[i.to(itype) for i in ix] for ix in idx_sets]
+    inp.offsets = [o.to(itype) for o in inp.offsets]
     ws = model.workspace(B)
     out = torch.empty(B, device=dev)
     argsets = [model.forward_args(inp.dense, idx, inp.offsets) for idx in idx_sets]
@@ -220,15 +241,22 @@ def run_workload(torch, dl, di, w, dev, args):
             graphs[i % nsets].replay()
 
         # the timed run replays graphs of G consecutive steps, so that one
-        # graph launch covers G forwards (the serving loop's form)
+        # graph launch covers G forwards (the serving loop's form); the K mod G
+        # steps left over run as one more graph of that many steps
         G = max(1, min(args.graph_steps, args.steps))
-        multi = torch.cuda.CUDAGraph()
-        stream.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(stream):
-            with torch.cuda.graph(multi, stream=stream):
-                for i in range(G):
-                    step(i)
-        torch.cuda.current_stream().wait_stream(stream)
+        rem = args.steps % G
+
+        def capture(n):
+            g = torch.cuda.CUDAGraph()
+            stream.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(stream):
+                with torch.cuda.graph(g, stream=stream):
+                    for i in range(n):
+                        step(i)
+            torch.cuda.current_stream().wait_stream(stream)
+            return g
+        multi = capture(G)
+        tail = capture(rem) if rem else None
         torch.cuda.synchronize()
 
     for i in range(args.warmup):
@@ -242,8 +270,8 @@ def run_workload(torch, dl, di, w, dev, args):
     else:
         for _ in range(args.steps // G):
             multi.replay()
-        for i in range(args.steps % G):
-            run(i)
+        if tail is not None:
+            tail.replay()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms = (t1 - t0) * 1e3 / args.steps
@@ -277,7 +305,7 @@ def run_workload(torch, dl, di, w, dev, args):
         del flush
 
     kernels = time_stages(torch, dl, model, inp, idx_sets, ws, w, args.kernel_reps,
-                          fused=model.packed is not None and path == "fused")
+                          fused=model.packed is not None and path == "fused", ib=args.index_bytes)
     traffic = counted_traffic(w.name)
     stages = [k for k in kernels if k["name"] != "fused_forward"]
     roof_layered = roofline(stages, dominant=True, traffic=traffic)
@@ -301,11 +329,11 @@ def run_workload(torch, dl, di, w, dev, args):
                 pct=pct, cold_us=cold, mlp_tflops=mlp_tf, path=path, layered=layered)
 
 
-def time_stages(torch, dl, model, inp, idx_sets, ws, w, reps, fused=False):
+def time_stages(torch, dl, model, inp, idx_sets, ws, w, reps, fused=False, ib=8):
     """Average duration of each kernel, launched alone on the current stream,
     with HIP events: the single-launch forward (when `fused`) and every stage
     of the layered path."""
-    stages = ([fused_algorithmic(w)] if fused else []) + algorithmic(w)
+    stages = ([fused_algorithmic(w, ib)] if fused else []) + algorithmic(w, ib)
     B, D = w.batch, w.dim
     P = w.n_pairs
     ldR = (D + P + 3) // 4 * 4
@@ -423,22 +451,90 @@ def roofline(kernels, dominant=True, traffic=None):
             "bytes_per_launch": k["bytes"]}
 
 
-def copy_ceiling(torch, dev, nbytes=1 << 30, reps=10):
-    """Read + write GB/s of a plain 1 GiB device-to-device copy (torch's copy kernel)."""
-    a = torch.ones(nbytes // 4, device=dev)
-    b = torch.empty_like(a)
-    for _ in range(3):
-        b.copy_(a)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+def _time_graph(torch, f, reps, rounds=3):
+    """Average microseconds of f() when `reps` calls are captured in one graph
+    and the graph is replayed `rounds` times between two events."""
+    for _ in range(2):
+        f()
     torch.cuda.synchronize()
+    stream = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            for _ in range(reps):
+                f()
+    torch.cuda.current_stream().wait_stream(stream)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
-    for _ in range(reps):
-        b.copy_(a)
+    for _ in range(rounds):
+        g.replay()
     e1.record()
     torch.cuda.synchronize()
-    gbps = 2 * nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
-    del a, b
-    return gbps
+    return e0.elapsed_time(e1) * 1e3 / (rounds * reps)
+
+
+def ceilings(torch, dl, dev, nbytes=2 << 30, gather_rows=1 << 21, dim=64):
+    """The library's own bandwidth ceilings: a sequential float4 read of 2 GiB
+    (bigger than every cache), and a gather of 2M random rows of 64 floats
+    from a 3.2 GB table (the access pattern of one-index bags; far bigger
+    than the 256 MB Infinity Cache)."""
+    src = torch.ones(nbytes // 4, device=dev)
+    us = _time_graph(torch, lambda: dl.probe_read_stream(src), reps=5)
+    read = nbytes / (us * 1e-6) / 1e9
+    del src
+    rows = (3200 << 20) // (dim * 4)
+    table = torch.ones((rows, dim), device=dev)
+    gen = torch.Generator(device=dev).manual_seed(11)
+    idx = torch.randint(0, rows, (gather_rows,), device=dev, generator=gen)
+    us_g = _time_graph(torch, lambda: dl.probe_gather_rows(table, idx), reps=5)
+    gbytes = gather_rows * (dim * 4 + 8)
+    gather = gbytes / (us_g * 1e-6) / 1e9
+    del table, idx
+    torch.cuda.empty_cache()
+    return {"read_stream_GBps": read, "read_stream_frac_of_peak": read / HBM_PEAK_GBPS,
+            "read_stream_bytes": nbytes, "gather_rows_GBps": gather,
+            "gather_rows_frac_of_peak": gather / HBM_PEAK_GBPS,
+            "gather_rows": gather_rows, "gather_row_bytes": dim * 4, "gather_bytes_incl_int64_index": gbytes}
+
+
+LARGE_CELLS = ((16384, 8), (16384, 16), (16384, 32))
+
+
+def large_cells(torch, dl, di, dev, args, ceil):
+    """dlrm_embbag_interact alone at batch 16384 with 8, 16 and 32 tables (the
+    sweep cells where the bag + interaction traffic is large enough to judge
+    against HBM bandwidth), 8 index sets rotating, replayed from a graph."""
+    out = {}
+    itype = torch.int32 if args.index_bytes == 4 else torch.int64
+    for B, T in LARGE_CELLS:
+        w = di.sweep(B, T)
+        inp = di.make_inputs(w, device=dev)
+        sets = [inp.indices] + [di.make_indices(w, device=dev, seed=di.BASE_SEED + 7919 * s) for s in range(1, 8)]
+        sets = [[i.to(itype) for i in ix] for ix in sets]
+        offs = [o.to(itype) for o in inp.offsets]
+        D, P = w.dim, w.n_pairs
+        R = torch.zeros((B, (D + P + 3) // 4 * 4), device=dev)
+        cnt = [0]
+
+        def emb():
+            cnt[0] += 1
+            dl.embbag_interact(inp.tables, sets[cnt[0] % 8], offs, R, concat_dense=False, out=R[:, D:])
+        us = _time_graph(torch, emb, reps=24)
+        ib = args.index_bytes
+        nbytes = B * T * w.bag * (D * 4 + ib) + B * T * ib + B * D * 4 + B * P * 4
+        gbps = nbytes / (us * 1e-6) / 1e9
+        cell = {"us": us, "bytes": nbytes, "GBps": gbps, "frac_of_peak": gbps / HBM_PEAK_GBPS}
+        if ceil:
+            cell["frac_of_read_ceiling"] = gbps / ceil["read_stream_GBps"]
+            cell["frac_of_gather_ceiling"] = gbps / ceil["gather_rows_GBps"]
+        out[f"{B}x{T}"] = cell
+        print(f"[bench] emb_interact {B}x{T}: {us:.1f} us, {gbps:.0f} GB/s", file=sys.stderr, flush=True)
+        del inp, sets, R
+        torch.cuda.empty_cache()
+    return out
 
 
 def copy_calibration(torch, dev, nbytes=512 << 20, reps=5):
@@ -473,27 +569,54 @@ def run_sweep(torch, dl, di, dev, args):
         json.dump(rows, f, indent=1)
 
 
-def cpu_baseline(w, seconds):
-    """The fp64 oracle (as it stands) on the host cores, on whole batches until `seconds` have passed."""
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.lower().startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(workloads, seconds):
+    """The fp64 oracle (as it stands) on the host: each workload's full batch,
+    on one thread and on all the threads this process may use (OMP_NUM_THREADS,
+    else the CPUs it is allowed to run on), whole forwards repeated until
+    `seconds` have passed."""
     import oracle
     import dlrm_inputs as di
-    import torch
     o = oracle.default()
-    threads = o.set_threads(int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1)))
-    n = min(w.batch, 512)
-    inp = di.make_inputs(w)
-    sub = di.subset(inp, torch.arange(n))
-    done = 0
-    t0 = time.perf_counter()
-    while True:
-        oracle.forward_inputs(sub, oracle=o)
-        done += n
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    return {"value": done / el, "unit": "samples/s", "cores": threads, "kind": "oracle",
-            "sample": f"{w.name}: the first {n} samples of the batch, forward repeated {done // n} times "
-                      f"in {el:.1f} s (fp64, OpenMP over samples)"}
+    allowed = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    n_all = int(os.environ.get("OMP_NUM_THREADS", 0)) or allowed
+
+    def rate(inp, threads):
+        used = o.set_threads(threads)
+        done, t0 = 0, time.perf_counter()
+        while True:
+            oracle.forward_inputs(inp, oracle=o)
+            done += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                return inp.workload.batch * done / el, used, done, el
+
+    per = {}
+    for w in workloads:
+        inp = di.make_inputs(w)
+        one, _, n1, t1 = rate(inp, 1)
+        many, used, nm, tm = rate(inp, n_all)
+        per[w.name] = {"samples_per_s_1thread": one, "samples_per_s_all": many, "threads_all": used,
+                       "us_per_forward_1thread": w.batch / one * 1e6, "us_per_forward_all": w.batch / many * 1e6,
+                       "forwards_timed": [n1, nm], "seconds": [t1, tm]}
+    first = per[workloads[0].name]
+    return {"value": first["samples_per_s_all"], "unit": "samples/s", "cores": first["threads_all"],
+            "kind": "oracle", "value_1thread": first["samples_per_s_1thread"],
+            "sample": f"{workloads[0].name}: the full batch of {workloads[0].batch} samples, whole fp64 forwards "
+                      f"(OpenMP over samples) repeated for at least {seconds:.0f} s, on "
+                      f"{first['threads_all']} threads and on 1",
+            "cpu_model": cpu_model(), "nproc": os.cpu_count(), "threads_allowed": allowed,
+            "workloads": per}
 
 
 if __name__ == "__main__":

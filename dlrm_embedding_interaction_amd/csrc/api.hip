@@ -21,15 +21,19 @@ inline int64_t n_pairs(int64_t f) { return f * (f - 1) / 2; }
 constexpr int64_t kIntLimit = (int64_t)1 << 30;  // sizes kept well inside int for kernel indexing
 
 // Per-table bag arguments shared by the bag entry points and the forward.
+// index_bytes 4: indices and offsets are int32, 8: int64.
 dlrm_status_t fill_tables(TableArgs& ta, int32_t T, int64_t B, int32_t D, const float* const* weights,
-                          const int64_t* rows, const int64_t* const* indices, const int64_t* n_indices,
-                          const int64_t* const* offsets, bool* aligned, bool* multi_hot) {
+                          const int64_t* rows, const void* const* indices, const int64_t* n_indices,
+                          const void* const* offsets, int32_t index_bytes, bool* aligned, bool* multi_hot) {
     memset(&ta, 0, sizeof(ta));
+    if (index_bytes != 4 && index_bytes != 8) return DLRM_E_SHAPE;
+    ta.idx32 = index_bytes == 4;
     bool al = (D % 4 == 0);
     bool mh = false;
     for (int32_t t = 0; t < T; ++t) {
         if (!weights[t] || !offsets[t]) return DLRM_E_NULL;
         if (rows[t] < 1 || n_indices[t] < 0 || n_indices[t] > kIntLimit * 64) return DLRM_E_SHAPE;
+        if (ta.idx32 && n_indices[t] > INT32_MAX) return DLRM_E_UNSUPPORTED;
         if (n_indices[t] > 0 && !indices[t]) return DLRM_E_NULL;
         ta.w[t] = weights[t];
         ta.idx[t] = indices[t];
@@ -40,6 +44,17 @@ dlrm_status_t fill_tables(TableArgs& ta, int32_t T, int64_t B, int32_t D, const 
     }
     *aligned = al;
     *multi_hot = mh;
+    return DLRM_OK;
+}
+
+// Table pointers of the stacked layout: table t is rows [row_base[t],
+// row_base[t] + rows[t]) of one (sum of rows, D) allocation.
+dlrm_status_t stacked_tables(const float* stacked, const int64_t* row_base, const int64_t* rows, int32_t T,
+                             int32_t D, const float** w) {
+    for (int32_t t = 0; t < T; ++t) {
+        if (row_base[t] < 0 || rows[t] < 1 || row_base[t] > ((int64_t)1 << 40)) return DLRM_E_SHAPE;
+        w[t] = stacked + row_base[t] * (int64_t)D;
+    }
     return DLRM_OK;
 }
 
@@ -104,19 +119,32 @@ DLRM_API const char* dlrm_status_string(dlrm_status_t s) {
 DLRM_API int32_t dlrm_abi_version(void) { return DLRM_ABI_VERSION; }
 
 DLRM_API dlrm_status_t dlrm_embbag_sum(int32_t num_tables, int64_t batch, int32_t dim, const float* const* weights,
-                                       const int64_t* rows, const int64_t* const* indices,
-                                       const int64_t* n_indices, const int64_t* const* offsets, float* out,
+                                       const int64_t* rows, const void* const* indices, const int64_t* n_indices,
+                                       const void* const* offsets, int32_t index_bytes, float* out,
                                        void* stream) {
     if (!weights || !rows || !indices || !n_indices || !offsets || !out) return DLRM_E_NULL;
     if (num_tables < 1 || batch < 1 || dim < 1) return DLRM_E_SHAPE;
     if (num_tables > DLRM_MAX_TABLES || dim > kMaxDim || batch > kIntLimit) return DLRM_E_UNSUPPORTED;
     TableArgs ta;
     bool aligned, multi_hot;
-    dlrm_status_t st = fill_tables(ta, num_tables, batch, dim, weights, rows, indices, n_indices, offsets, &aligned,
-                                   &multi_hot);
+    dlrm_status_t st = fill_tables(ta, num_tables, batch, dim, weights, rows, indices, n_indices, offsets,
+                                   index_bytes, &aligned, &multi_hot);
     if (st != DLRM_OK) return st;
     aligned = aligned && al16(out);
     return from_hip(launch_embbag_sum(ta, num_tables, dim, batch, aligned, multi_hot, out, (hipStream_t)stream));
+}
+
+DLRM_API dlrm_status_t dlrm_embbag_sum_stacked(int32_t num_tables, int64_t batch, int32_t dim, const float* stacked,
+                                               const int64_t* row_base, const int64_t* rows,
+                                               const void* const* indices, const int64_t* n_indices,
+                                               const void* const* offsets, int32_t index_bytes, float* out,
+                                               void* stream) {
+    if (!stacked || !row_base || !rows) return DLRM_E_NULL;
+    if (num_tables < 1 || dim < 1) return DLRM_E_SHAPE;
+    if (num_tables > DLRM_MAX_TABLES) return DLRM_E_UNSUPPORTED;
+    const float* w[DLRM_MAX_TABLES];
+    if (stacked_tables(stacked, row_base, rows, num_tables, dim, w) != DLRM_OK) return DLRM_E_SHAPE;
+    return dlrm_embbag_sum(num_tables, batch, dim, w, rows, indices, n_indices, offsets, index_bytes, out, stream);
 }
 
 DLRM_API dlrm_status_t dlrm_embbag(int32_t num_tables, int64_t batch, int32_t dim, const float* const* weights,
@@ -168,9 +196,10 @@ DLRM_API dlrm_status_t dlrm_interact_lower_tri(int64_t batch, int32_t num_tables
 
 DLRM_API dlrm_status_t dlrm_embbag_interact(int32_t num_tables, int64_t batch, int32_t dim,
                                             const float* const* weights, const int64_t* rows,
-                                            const int64_t* const* indices, const int64_t* n_indices,
-                                            const int64_t* const* offsets, const float* x, int64_t ld_x, float* out,
-                                            int64_t ld_out, int32_t concat_dense, void* stream) {
+                                            const void* const* indices, const int64_t* n_indices,
+                                            const void* const* offsets, int32_t index_bytes, const float* x,
+                                            int64_t ld_x, float* out, int64_t ld_out, int32_t concat_dense,
+                                            void* stream) {
     if (!weights || !rows || !indices || !n_indices || !offsets || !x || !out) return DLRM_E_NULL;
     if (num_tables < 1 || batch < 1 || dim < 1 || ld_x < dim) return DLRM_E_SHAPE;
     if (num_tables > DLRM_MAX_TABLES || dim > kMaxDim || batch > kIntLimit) return DLRM_E_UNSUPPORTED;
@@ -179,8 +208,8 @@ DLRM_API dlrm_status_t dlrm_embbag_interact(int32_t num_tables, int64_t batch, i
     if (ld_out < (concat_dense ? dim + P : P)) return DLRM_E_SHAPE;
     TableArgs ta;
     bool aligned, multi_hot;
-    dlrm_status_t st = fill_tables(ta, num_tables, batch, dim, weights, rows, indices, n_indices, offsets, &aligned,
-                                   &multi_hot);
+    dlrm_status_t st = fill_tables(ta, num_tables, batch, dim, weights, rows, indices, n_indices, offsets,
+                                   index_bytes, &aligned, &multi_hot);
     if (st != DLRM_OK) return st;
     aligned = aligned && (ld_x % 4 == 0) && al16(x);
     return from_hip(launch_interact(&ta, nullptr, num_tables, dim, batch, aligned, multi_hot, x, ld_x, out, ld_out,
@@ -206,20 +235,34 @@ DLRM_API size_t dlrm_forward_workspace_bytes(const dlrm_model_t* m, int64_t batc
 
 namespace {
 
+// The model's table pointers: emb_w, or the stacked layout when emb_w is NULL.
+dlrm_status_t model_tables(const dlrm_model_t* m, const float** w) {
+    if (!m->rows) return DLRM_E_NULL;
+    if (m->emb_w) {
+        for (int32_t t = 0; t < m->num_tables; ++t) w[t] = m->emb_w[t];
+        return DLRM_OK;
+    }
+    if (!m->emb_stacked || !m->emb_row_base) return DLRM_E_NULL;
+    return stacked_tables(m->emb_stacked, m->emb_row_base, m->rows, m->num_tables, m->emb_dim, w);
+}
+
 // Checks shared by every forward entry point; fills the table arguments.
-dlrm_status_t forward_args(const dlrm_model_t* m, int64_t batch, const float* dense, const int64_t* const* indices,
-                           const int64_t* n_indices, const int64_t* const* offsets, const float* out,
-                           TableArgs& ta, bool* aligned, bool* multi_hot) {
+dlrm_status_t forward_args(const dlrm_model_t* m, int64_t batch, const float* dense, const void* const* indices,
+                           const int64_t* n_indices, const void* const* offsets, int32_t index_bytes,
+                           const float* out, TableArgs& ta, bool* aligned, bool* multi_hot) {
     dlrm_status_t st = validate_model(m, batch);
     if (st != DLRM_OK) return st;
     if (!dense || !indices || !n_indices || !offsets || !out) return DLRM_E_NULL;
-    if (!m->rows || !m->emb_w || !m->bot_w || !m->bot_b || !m->top_w || !m->top_b) return DLRM_E_NULL;
+    if (!m->rows || !m->bot_w || !m->bot_b || !m->top_w || !m->top_b) return DLRM_E_NULL;
     for (int32_t l = 0; l + 1 < m->n_bot; ++l)
         if (!m->bot_w[l] || !m->bot_b[l]) return DLRM_E_NULL;
     for (int32_t l = 0; l + 1 < m->n_top; ++l)
         if (!m->top_w[l] || !m->top_b[l]) return DLRM_E_NULL;
-    return fill_tables(ta, m->num_tables, batch, m->emb_dim, m->emb_w, m->rows, indices, n_indices, offsets, aligned,
-                       multi_hot);
+    const float* w[DLRM_MAX_TABLES];
+    st = model_tables(m, w);
+    if (st != DLRM_OK) return st;
+    return fill_tables(ta, m->num_tables, batch, m->emb_dim, w, m->rows, indices, n_indices, offsets, index_bytes,
+                       aligned, multi_hot);
 }
 
 // Segments of the packed tail (see SmallBlock).
@@ -293,9 +336,10 @@ size_t packed_floats(const dlrm_model_t* m) {
 // Shape-only check of the single-launch path for a model (tables' alignment
 // included); used by the packing calls.
 bool model_fits_fused(const dlrm_model_t* m) {
-    if (validate_model(m, 1) != DLRM_OK || !m->emb_w) return false;
+    const float* w[DLRM_MAX_TABLES];
+    if (validate_model(m, 1) != DLRM_OK || model_tables(m, w) != DLRM_OK) return false;
     bool aligned = (m->emb_dim % 4 == 0);
-    for (int32_t t = 0; t < m->num_tables; ++t) aligned = aligned && m->emb_w[t] && al16(m->emb_w[t]);
+    for (int32_t t = 0; t < m->num_tables; ++t) aligned = aligned && w[t] && al16(w[t]);
     TableArgs ta;
     memset(&ta, 0, sizeof(ta));
     FusedArgs fa;
@@ -386,12 +430,13 @@ dlrm_status_t forward_layered(const dlrm_model_t* m, int64_t batch, const float*
 }  // namespace
 
 DLRM_API dlrm_status_t dlrm_forward_layered(const dlrm_model_t* m, int64_t batch, const float* dense,
-                                            const int64_t* const* indices, const int64_t* n_indices,
-                                            const int64_t* const* offsets, float* out, void* workspace,
-                                            size_t ws_bytes, void* stream) {
+                                            const void* const* indices, const int64_t* n_indices,
+                                            const void* const* offsets, int32_t index_bytes, float* out,
+                                            void* workspace, size_t ws_bytes, void* stream) {
     TableArgs ta;
     bool aligned, multi_hot;
-    dlrm_status_t st = forward_args(m, batch, dense, indices, n_indices, offsets, out, ta, &aligned, &multi_hot);
+    dlrm_status_t st = forward_args(m, batch, dense, indices, n_indices, offsets, index_bytes, out, ta, &aligned,
+                                    &multi_hot);
     if (st != DLRM_OK) return st;
     return forward_layered(m, batch, dense, out, ta, aligned, multi_hot, workspace, ws_bytes, (hipStream_t)stream);
 }
@@ -435,11 +480,13 @@ DLRM_API dlrm_status_t dlrm_pack_weights(const dlrm_model_t* m, float* packed, s
 }
 
 DLRM_API dlrm_status_t dlrm_forward_fused(const dlrm_model_t* m, int64_t batch, const float* dense,
-                                          const int64_t* const* indices, const int64_t* n_indices,
-                                          const int64_t* const* offsets, float* out, void* stream) {
+                                          const void* const* indices, const int64_t* n_indices,
+                                          const void* const* offsets, int32_t index_bytes, float* out,
+                                          void* stream) {
     TableArgs ta;
     bool aligned, multi_hot;
-    dlrm_status_t st = forward_args(m, batch, dense, indices, n_indices, offsets, out, ta, &aligned, &multi_hot);
+    dlrm_status_t st = forward_args(m, batch, dense, indices, n_indices, offsets, index_bytes, out, ta, &aligned,
+                                    &multi_hot);
     if (st != DLRM_OK) return st;
     FusedArgs fa;
     if (!fused_args(m, batch, dense, out, ta, aligned, m->packed_w, fa)) return DLRM_E_UNSUPPORTED;
@@ -457,12 +504,13 @@ DLRM_API int32_t dlrm_forward_path(const dlrm_model_t* m, int64_t batch) {
 }
 
 DLRM_API dlrm_status_t dlrm_forward(const dlrm_model_t* m, int64_t batch, const float* dense,
-                                    const int64_t* const* indices, const int64_t* n_indices,
-                                    const int64_t* const* offsets, float* out, void* workspace, size_t ws_bytes,
-                                    void* stream) {
+                                    const void* const* indices, const int64_t* n_indices,
+                                    const void* const* offsets, int32_t index_bytes, float* out, void* workspace,
+                                    size_t ws_bytes, void* stream) {
     TableArgs ta;
     bool aligned, multi_hot;
-    dlrm_status_t st = forward_args(m, batch, dense, indices, n_indices, offsets, out, ta, &aligned, &multi_hot);
+    dlrm_status_t st = forward_args(m, batch, dense, indices, n_indices, offsets, index_bytes, out, ta, &aligned,
+                                    &multi_hot);
     if (st != DLRM_OK) return st;
     Plan p;
     make_plan(m, batch, &p);
@@ -475,14 +523,16 @@ DLRM_API dlrm_status_t dlrm_forward(const dlrm_model_t* m, int64_t batch, const 
 }
 
 DLRM_API dlrm_status_t dlrm_embbag_check_indices(int32_t num_tables, int64_t batch, const int64_t* rows,
-                                                 const int64_t* const* indices, const int64_t* n_indices,
-                                                 const int64_t* const* offsets, int32_t* bad_count_device,
-                                                 void* stream) {
+                                                 const void* const* indices, const int64_t* n_indices,
+                                                 const void* const* offsets, int32_t index_bytes,
+                                                 int32_t* bad_count_device, void* stream) {
     if (!rows || !indices || !n_indices || !offsets || !bad_count_device) return DLRM_E_NULL;
     if (num_tables < 1 || batch < 1) return DLRM_E_SHAPE;
+    if (index_bytes != 4 && index_bytes != 8) return DLRM_E_SHAPE;
     if (num_tables > DLRM_MAX_TABLES) return DLRM_E_UNSUPPORTED;
     CheckArgs ca;
     memset(&ca, 0, sizeof(ca));
+    ca.idx32 = index_bytes == 4;
     for (int32_t t = 0; t < num_tables; ++t) {
         if (!offsets[t]) return DLRM_E_NULL;
         if (n_indices[t] < 0) return DLRM_E_SHAPE;
@@ -499,4 +549,21 @@ DLRM_API dlrm_status_t dlrm_pair_index_map(int32_t n_feat, int32_t* i_out, int32
     if (!i_out || !j_out) return DLRM_E_NULL;
     if (n_feat < 2 || n_feat > 4096) return DLRM_E_SHAPE;
     return from_hip(launch_pair_index_map(n_feat, i_out, j_out, (hipStream_t)stream));
+}
+
+DLRM_API int64_t dlrm_probe_sink_floats(void) { return probe_blocks(); }
+
+DLRM_API dlrm_status_t dlrm_probe_read_stream(const float* src, int64_t n_floats, float* sink, void* stream) {
+    if (!src || !sink) return DLRM_E_NULL;
+    if (n_floats < 4 || n_floats % 4 != 0) return DLRM_E_SHAPE;
+    if (!al16(src)) return DLRM_E_SHAPE;
+    return from_hip(launch_read_stream(src, n_floats, sink, (hipStream_t)stream));
+}
+
+DLRM_API dlrm_status_t dlrm_probe_gather_rows(const float* table, int64_t rows, int32_t dim, const int64_t* idx,
+                                              int64_t n, float* sink, void* stream) {
+    if (!table || !idx || !sink) return DLRM_E_NULL;
+    if (rows < 1 || n < 1 || dim < 16 || dim > 256 || (dim & (dim - 1)) != 0) return DLRM_E_SHAPE;
+    if (!al16(table)) return DLRM_E_SHAPE;
+    return from_hip(launch_gather_rows(table, dim, idx, n, sink, (hipStream_t)stream));
 }

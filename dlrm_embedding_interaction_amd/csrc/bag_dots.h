@@ -39,24 +39,28 @@ __device__ __forceinline__ void gather_bags(const TableArgs& ta, int T, int D, i
                                             typename Vec<VEC>::T (&acc)[U][C]) {
     using V = Vec<VEC>;
     const float* wp[U];
-    const int64_t* ip[U];
+    const void* ip[U];
+    int64_t ks[U];
     int len[U];
     int maxlen = 0;
+    const int i32 = ta.idx32;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         len[u] = 0;
         wp[u] = nullptr;
         ip[u] = nullptr;
+        ks[u] = 0;
         if (q[u] >= 0) {
             const int sl = q[u] / T;
             const int t = q[u] - sl * T;
             const int64_t b = b_base + sl;
-            const int64_t* off = ta.off[t];
-            const int64_t s = off[b];
-            const int64_t e = (b + 1 < B) ? off[b + 1] : ta.nidx[t];
+            const void* off = ta.off[t];
+            const int64_t s = ld_index(off, b, i32);
+            const int64_t e = (b + 1 < B) ? ld_index(off, b + 1, i32) : ta.nidx[t];
             len[u] = (int)(e - s);
             wp[u] = ta.w[t];
-            ip[u] = ta.idx[t] + s;
+            ip[u] = ta.idx[t];
+            ks[u] = s;
         }
         maxlen = max(maxlen, len[u]);
 #pragma unroll
@@ -67,7 +71,7 @@ __device__ __forceinline__ void gather_bags(const TableArgs& ta, int T, int D, i
 #pragma unroll
         for (int rr = 0; rr < R; ++rr)
 #pragma unroll
-            for (int u = 0; u < U; ++u) row[rr][u] = (r0 + rr < len[u]) ? ip[u][r0 + rr] : -1;
+            for (int u = 0; u < U; ++u) row[rr][u] = (r0 + rr < len[u]) ? ld_index(ip[u], ks[u] + r0 + rr, i32) : -1;
         typename V::T v[R][U][C];
 #pragma unroll
         for (int rr = 0; rr < R; ++rr)

@@ -14,13 +14,22 @@ constexpr int kWave = 64;          // CDNA wavefront width
 constexpr int kBlock = 256;        // threads per block of the gather / interaction kernels
 
 // Per-table pointers of one multi-table bag launch, passed by value in the
-// kernel arguments (64 tables x 4 x 8 bytes = 2 KiB).
+// kernel arguments (64 tables x 4 x 8 bytes = 2 KiB).  Indices and offsets
+// are all int32 (idx32 != 0) or all int64.
 struct TableArgs {
     const float* w[DLRM_MAX_TABLES];
-    const int64_t* idx[DLRM_MAX_TABLES];
-    const int64_t* off[DLRM_MAX_TABLES];
+    const void* idx[DLRM_MAX_TABLES];
+    const void* off[DLRM_MAX_TABLES];
     int64_t nidx[DLRM_MAX_TABLES];
+    int idx32;
 };
+
+// Element k of an index or offset array of the launch's width (a branch on a
+// kernel argument, the same for every lane).
+__device__ __forceinline__ int64_t ld_index(const void* base, int64_t k, int idx32) {
+    if (idx32) return (int64_t) static_cast<const int32_t*>(base)[k];
+    return static_cast<const int64_t*>(base)[k];
+}
 
 // ---- lane-group sums ---------------------------------------------------------
 // Sum of v over aligned groups of G lanes (G a power of two <= 64); every lane

@@ -50,10 +50,11 @@ struct FusedArgs {
 
 // Arguments of the device-side bag-data check.
 struct CheckArgs {
-    const int64_t* idx[DLRM_MAX_TABLES];
-    const int64_t* off[DLRM_MAX_TABLES];
+    const void* idx[DLRM_MAX_TABLES];
+    const void* off[DLRM_MAX_TABLES];
     int64_t nidx[DLRM_MAX_TABLES];
     int64_t rows[DLRM_MAX_TABLES];
+    int idx32;
 };
 
 // Arguments of the general bag kernel (3 KiB of kernel arguments).
@@ -111,6 +112,14 @@ hipError_t launch_pack_small(const SmallBlock& sb, float* dst, hipStream_t s);
 hipError_t launch_check_indices(const CheckArgs& ca, int T, int64_t B, int32_t* bad, hipStream_t s);
 
 hipError_t launch_pair_index_map(int F, int32_t* i_out, int32_t* j_out, hipStream_t s);
+
+// Measurement kernels: a sequential float4 read of n_floats (a multiple of 4)
+// and a gather of n rows of `dim` floats (dim / 4 in {4, 8, 16, 32, 64}) picked
+// by idx; sink holds probe_blocks() floats and is written only in theory.
+int probe_blocks();
+hipError_t launch_read_stream(const float* src, int64_t n_floats, float* sink, hipStream_t s);
+hipError_t launch_gather_rows(const float* table, int dim, const int64_t* idx, int64_t n, float* sink,
+                              hipStream_t s);
 
 // y = act(x W^T + bias): MFMA for N > 1, a dot-product kernel for N == 1.
 hipError_t launch_linear(int64_t M, int64_t N, int64_t K, const float* x, int64_t ld_x, const float* W,

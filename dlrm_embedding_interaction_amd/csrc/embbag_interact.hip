@@ -166,12 +166,12 @@ __global__ __launch_bounds__(kBlock) void check_indices_kernel(CheckArgs ca, int
         const int64_t rows = ca.rows[t];
         const int64_t n = ca.nidx[t];
         for (int64_t k = (int64_t)blockIdx.x * kBlock + threadIdx.x; k < n; k += stride) {
-            const int64_t v = ca.idx[t][k];
+            const int64_t v = ld_index(ca.idx[t], k, ca.idx32);
             local += (v < 0 || v >= rows);
         }
         for (int64_t b = (int64_t)blockIdx.x * kBlock + threadIdx.x; b < B; b += stride) {
-            const int64_t s = ca.off[t][b];
-            const int64_t e = (b + 1 < B) ? ca.off[t][b + 1] : n;
+            const int64_t s = ld_index(ca.off[t], b, ca.idx32);
+            const int64_t e = (b + 1 < B) ? ld_index(ca.off[t], b + 1, ca.idx32) : n;
             local += (s < 0 || s > e || e > n);
         }
     }

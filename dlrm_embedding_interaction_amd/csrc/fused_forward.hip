@@ -25,6 +25,8 @@
 //
 // Samples are independent, so blocks never communicate; the weights of one
 // forward (a few MB) stay resident in every XCD's L2.
+#include <mutex>
+
 #include "dlrm_device.h"
 #include "dlrm_internal.h"
 #include "rowvec.h"
@@ -439,16 +441,30 @@ hipError_t launch_pack_small(const SmallBlock& sb, float* dst, hipStream_t s) {
     return hipGetLastError();
 }
 
+// The kernel's LDS limit is raised to the whole 160 KiB once per kernel
+// instantiation and device, by whichever thread launches it there first
+// (std::call_once: concurrent first launches wait for that one call).
+template <typename Kernel>
+static hipError_t allow_full_lds(Kernel* k) {
+    constexpr int kMaxDevices = 64;
+    static std::once_flag once[kMaxDevices];
+    static hipError_t result[kMaxDevices];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    auto set = [&] {
+        return hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kFusedMaxLds);
+    };
+    if (dev < 0 || dev >= kMaxDevices) return set();
+    std::call_once(once[dev], [&] { result[dev] = set(); });
+    return result[dev];
+}
+
 template <int S, int G, int U, int R, int RT>
 static hipError_t launch_fused_t(const FusedArgs& fa, hipStream_t s) {
     const size_t lds = fused_lds_bytes(fa, S);
-    static bool attr_set = false;  // one attribute call per instantiation and process
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)fused_forward_kernel<S, G, U, R, RT>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)kFusedMaxLds);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    hipError_t e = allow_full_lds(fused_forward_kernel<S, G, U, R, RT>);
+    if (e != hipSuccess) return e;
     const int64_t blocks = (fa.B + S - 1) / S;
     hipLaunchKernelGGL((fused_forward_kernel<S, G, U, R, RT>), dim3((unsigned)blocks), dim3(kFusedThreads), lds, s,
                        fa);

@@ -254,7 +254,6 @@ def subset(inp: Inputs, rows: torch.Tensor, compact_tables: bool = False) -> Inp
     selection, used to check sampled outputs of a large batch.
     """
     rows = rows.to("cpu")
-    B = inp.workload.batch
     new_idx, new_off, new_tab = [], [], []
     for tab, idx, off in zip(inp.tables, inp.indices, inp.offsets):
         off_c = off.to("cpu")
@@ -263,8 +262,11 @@ def subset(inp: Inputs, rows: torch.Tensor, compact_tables: bool = False) -> Inp
         ends = torch.cat([off_c[1:], torch.tensor([n], dtype=torch.int64)])
         s, e = off_c[rows], ends[rows]
         lens = e - s
-        parts = [torch.arange(a, b, dtype=torch.int64) for a, b in zip(s.tolist(), e.tolist())]
-        take = torch.cat(parts) if parts else torch.zeros(0, dtype=torch.int64)
+        # positions of every selected bag's indices, bag after bag, each bag's in order
+        total = int(lens.sum())
+        starts = torch.cumsum(lens, 0) - lens
+        take = (torch.repeat_interleave(s, lens) +
+                torch.arange(total, dtype=torch.int64) - torch.repeat_interleave(starts, lens))
         sel = idx_c[take]
         if compact_tables:
             uniq, inv = torch.unique(sel, return_inverse=True)
@@ -275,10 +277,7 @@ def subset(inp: Inputs, rows: torch.Tensor, compact_tables: bool = False) -> Inp
         else:
             new_tab.append(tab.to("cpu"))
             new_idx.append(sel)
-        o = torch.zeros(rows.numel(), dtype=torch.int64)
-        if rows.numel() > 1:
-            o[1:] = torch.cumsum(lens[:-1], 0)
-        new_off.append(o)
+        new_off.append(starts)
     w = inp.workload.with_batch(int(rows.numel()))
     cpu = lambda xs: [x.to("cpu") for x in xs]
     return Inputs(w, inp.dense.to("cpu")[rows], new_tab, new_idx, new_off,

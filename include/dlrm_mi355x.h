@@ -22,8 +22,12 @@
  *    read during the call only and never kept.  The library allocates
  *    nothing and frees nothing.
  *  - Layout: row-major, C-contiguous unless an explicit leading dimension
- *    (ld_*) is given, in elements.  Floating point is IEEE fp32; indices and
- *    offsets are int64 (PyTorch's torch.long).
+ *    (ld_*) is given, in elements.  Floating point is IEEE fp32.  Indices and
+ *    offsets are integers of the width `index_bytes` gives: 8 (int64, PyTorch's
+ *    torch.long) or 4 (int32, the width the pages' megakernel narrows them to:
+ *    DlrmMegaKernel struct fields in dlrm_megakernel.rs, "luminal compare
+ *    dlrm-fused-kernels...dlrm-pt2-megakernel"); one width for all tables of a
+ *    call, indices and offsets alike.  Other widths give DLRM_E_SHAPE.
  *  - Streams: `stream` is a hipStream_t passed as void* (NULL = the default
  *    stream).  Every call only enqueues work on that stream: there is no host
  *    or device synchronisation, no host<->device copy and no allocation, so
@@ -77,7 +81,13 @@ typedef enum dlrm_status {
  *   ln_top[n_top-1]    == 1 (binary classifier)
  *   bot_w[l]           (ln_bot[l+1], ln_bot[l]) nn.Linear layout, bot_b[l] (ln_bot[l+1])
  *   top_w[l]           (ln_top[l+1], ln_top[l]),                top_b[l] (ln_top[l+1])
- *   emb_w[t]           (rows[t], emb_dim)
+ *   emb_w[t]           (rows[t], emb_dim); or NULL, and then the tables are
+ *                      stacked: table t is rows [emb_row_base[t],
+ *                      emb_row_base[t] + rows[t]) of the one device allocation
+ *                      emb_stacked (sum of rows, emb_dim), the pre-stacked
+ *                      weight of StackedEmbeddingBagKernel ("luminal compare
+ *                      asglover/modal_ci_ready...vanilla-pytorch", cuda_lite
+ *                      kernels)
  *   packed_w           NULL, or device memory holding the weights and biases
  *                      in the order the single-launch forward reads them,
  *                      written by dlrm_pack_weights from the arrays above
@@ -98,6 +108,8 @@ typedef struct dlrm_model {
     const float* const* top_w;
     const float* const* top_b;
     const float* packed_w;
+    const float* emb_stacked;
+    const int64_t* emb_row_base;
 } dlrm_model_t;
 
 /*
@@ -120,16 +132,33 @@ typedef struct dlrm_model {
  *               the vector path)
  *   weights     host[T] of device pointers, table t is (rows[t], dim)
  *   rows        host[T], rows[t] >= 1 (used by the checked call only)
- *   indices     host[T] of device pointers, (n_indices[t]) int64
- *   n_indices   host[T], >= 0
- *   offsets     host[T] of device pointers, (batch) int64
+ *   indices     host[T] of device pointers, (n_indices[t]) integers
+ *   n_indices   host[T], >= 0 (<= INT32_MAX with 4-byte indices)
+ *   offsets     host[T] of device pointers, (batch) integers
+ *   index_bytes 4 or 8, the width of indices and offsets
  *   out         device (batch, T, dim) fp32, written completely
  * Bag sums are accumulated in fp32 in increasing k.
  */
 dlrm_status_t dlrm_embbag_sum(int32_t num_tables, int64_t batch, int32_t dim,
                               const float* const* weights, const int64_t* rows,
-                              const int64_t* const* indices, const int64_t* n_indices,
-                              const int64_t* const* offsets, float* out, void* stream);
+                              const void* const* indices, const int64_t* n_indices,
+                              const void* const* offsets, int32_t index_bytes, float* out,
+                              void* stream);
+
+/*
+ * dlrm_embbag_sum_stacked -- dlrm_embbag_sum over tables stacked in one
+ * allocation, the pre-stacked weight layout of StackedEmbeddingBagKernel
+ * ("luminal compare asglover/modal_ci_ready...vanilla-pytorch", cuda_lite
+ * kernels): table t is rows [row_base[t], row_base[t] + rows[t]) of the
+ * device array `stacked` (sum of rows, dim); indices stay relative to their
+ * own table.  row_base and rows are host[T], row_base[t] >= 0.  Other
+ * arguments, output and errors as dlrm_embbag_sum.
+ */
+dlrm_status_t dlrm_embbag_sum_stacked(int32_t num_tables, int64_t batch, int32_t dim,
+                                      const float* stacked, const int64_t* row_base,
+                                      const int64_t* rows, const void* const* indices,
+                                      const int64_t* n_indices, const void* const* offsets,
+                                      int32_t index_bytes, float* out, void* stream);
 
 /* Pooling modes of dlrm_embbag. */
 #define DLRM_BAG_SUM 0
@@ -220,9 +249,10 @@ dlrm_status_t dlrm_interact_lower_tri(int64_t batch, int32_t num_tables, int32_t
  */
 dlrm_status_t dlrm_embbag_interact(int32_t num_tables, int64_t batch, int32_t dim,
                                    const float* const* weights, const int64_t* rows,
-                                   const int64_t* const* indices, const int64_t* n_indices,
-                                   const int64_t* const* offsets, const float* x, int64_t ld_x,
-                                   float* out, int64_t ld_out, int32_t concat_dense, void* stream);
+                                   const void* const* indices, const int64_t* n_indices,
+                                   const void* const* offsets, int32_t index_bytes, const float* x,
+                                   int64_t ld_x, float* out, int64_t ld_out, int32_t concat_dense,
+                                   void* stream);
 
 /*
  * dlrm_linear_bias_act -- y = act(x W^T + bias), i.e. addmm(bias, x, W.t())
@@ -263,9 +293,10 @@ size_t dlrm_forward_workspace_bytes(const dlrm_model_t* m, int64_t batch);
  *   m          host model descriptor (validated: dlrm_megakernel.rs validate)
  *   batch      B >= 1
  *   dense      device (B, ln_bot[0]) fp32
- *   indices    host[T] of device pointers (n_indices[t]) int64
+ *   indices    host[T] of device pointers (n_indices[t]) integers
  *   n_indices  host[T]
- *   offsets    host[T] of device pointers (B) int64, as dlrm_embbag_sum
+ *   offsets    host[T] of device pointers (B) integers, as dlrm_embbag_sum
+ *   index_bytes  4 or 8, the width of indices and offsets
  *   out        device (B) fp32 probabilities
  *   workspace  device, >= dlrm_forward_workspace_bytes(m, B), 256-byte aligned
  * Enqueues either one kernel (the single-launch path of dlrm_forward_fused,
@@ -279,9 +310,9 @@ size_t dlrm_forward_workspace_bytes(const dlrm_model_t* m, int64_t batch);
  * results agree to rounding.
  */
 dlrm_status_t dlrm_forward(const dlrm_model_t* m, int64_t batch, const float* dense,
-                           const int64_t* const* indices, const int64_t* n_indices,
-                           const int64_t* const* offsets, float* out, void* workspace,
-                           size_t ws_bytes, void* stream);
+                           const void* const* indices, const int64_t* n_indices,
+                           const void* const* offsets, int32_t index_bytes, float* out,
+                           void* workspace, size_t ws_bytes, void* stream);
 
 /*
  * dlrm_forward_path -- which path dlrm_forward takes for model m and `batch`
@@ -300,9 +331,9 @@ int32_t dlrm_forward_path(const dlrm_model_t* m, int64_t batch);
  * errors as dlrm_forward.
  */
 dlrm_status_t dlrm_forward_layered(const dlrm_model_t* m, int64_t batch, const float* dense,
-                                   const int64_t* const* indices, const int64_t* n_indices,
-                                   const int64_t* const* offsets, float* out, void* workspace,
-                                   size_t ws_bytes, void* stream);
+                                   const void* const* indices, const int64_t* n_indices,
+                                   const void* const* offsets, int32_t index_bytes, float* out,
+                                   void* workspace, size_t ws_bytes, void* stream);
 
 /*
  * dlrm_pack_weights_bytes -- bytes of the packed weights of model m for the
@@ -338,8 +369,9 @@ dlrm_status_t dlrm_pack_weights(const dlrm_model_t* m, float* packed, size_t byt
  * 160 KiB.
  */
 dlrm_status_t dlrm_forward_fused(const dlrm_model_t* m, int64_t batch, const float* dense,
-                                 const int64_t* const* indices, const int64_t* n_indices,
-                                 const int64_t* const* offsets, float* out, void* stream);
+                                 const void* const* indices, const int64_t* n_indices,
+                                 const void* const* offsets, int32_t index_bytes, float* out,
+                                 void* stream);
 
 /*
  * dlrm_embbag_check_indices -- validate the bag data of dlrm_embbag_sum on the
@@ -349,9 +381,9 @@ dlrm_status_t dlrm_forward_fused(const dlrm_model_t* m, int64_t batch, const flo
  * stream has finished.  Returns DLRM_OK when the check was enqueued.
  */
 dlrm_status_t dlrm_embbag_check_indices(int32_t num_tables, int64_t batch, const int64_t* rows,
-                                        const int64_t* const* indices, const int64_t* n_indices,
-                                        const int64_t* const* offsets, int32_t* bad_count_device,
-                                        void* stream);
+                                        const void* const* indices, const int64_t* n_indices,
+                                        const void* const* offsets, int32_t index_bytes,
+                                        int32_t* bad_count_device, void* stream);
 
 /*
  * dlrm_pair_index_map -- write the interaction kernels' own flat-pair-index
@@ -363,12 +395,30 @@ dlrm_status_t dlrm_embbag_check_indices(int32_t num_tables, int64_t batch, const
  */
 dlrm_status_t dlrm_pair_index_map(int32_t n_feat, int32_t* i_out, int32_t* j_out, void* stream);
 
+/*
+ * Measurement helpers (not part of the forward).  They set the bandwidth
+ * ceilings the bag and interaction kernels are reported against, from kernels
+ * of this library rather than a vendor copy.  Both only read memory; sink is
+ * device memory of dlrm_probe_sink_floats() floats that is written only if the
+ * data read sums to an impossible value.  Asynchronous on `stream`.
+ *
+ * dlrm_probe_read_stream -- reads n_floats (a multiple of 4, src 16-byte
+ *   aligned) of device memory once, sequentially, 16 bytes per lane.
+ * dlrm_probe_gather_rows -- reads the n rows idx[0..n) (int64, each in
+ *   [0, rows)) of the (rows, dim) fp32 table, dim in {16, 32, 64, 128, 256},
+ *   table 16-byte aligned: the access pattern of one-index bags.
+ */
+int64_t dlrm_probe_sink_floats(void);
+dlrm_status_t dlrm_probe_read_stream(const float* src, int64_t n_floats, float* sink, void* stream);
+dlrm_status_t dlrm_probe_gather_rows(const float* table, int64_t rows, int32_t dim, const int64_t* idx,
+                                     int64_t n, float* sink, void* stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* dlrm_status_string(dlrm_status_t status);
 
 /* ABI version of this header, bumped on any incompatible change. */
 int32_t dlrm_abi_version(void);
-#define DLRM_ABI_VERSION 2
+#define DLRM_ABI_VERSION 3
 
 #ifdef __cplusplus
 }

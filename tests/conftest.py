@@ -35,5 +35,5 @@ def orc():
     """The fp64 oracle (built with gcc on first use if its library is missing)."""
     import oracle
     o = oracle.default()
-    o.set_threads(min(8, os.cpu_count() or 1))
+    o.set_threads(int(os.environ.get("OMP_NUM_THREADS", 0)) or min(8, os.cpu_count() or 1))
     return o

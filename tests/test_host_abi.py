@@ -92,9 +92,9 @@ def test_invalid_models_are_rejected(lib, ln_bot, ln_top, T, D, B):
     assert lib.dlrm_forward_workspace_bytes(ctypes.byref(m), B) == 0
     one = dl._ptrs([])
     for fn in (lib.dlrm_forward, lib.dlrm_forward_layered):
-        rc = fn(ctypes.byref(m), B, 4096, one, dl._i64s([1] * T), one, 4096, 4096, 1 << 30, None)
+        rc = fn(ctypes.byref(m), B, 4096, one, dl._i64s([1] * T), one, 8, 4096, 4096, 1 << 30, None)
         assert rc == dl.DLRM_E_SHAPE
-    rc = lib.dlrm_forward_fused(ctypes.byref(m), B, 4096, one, dl._i64s([1] * T), one, 4096, None)
+    rc = lib.dlrm_forward_fused(ctypes.byref(m), B, 4096, one, dl._i64s([1] * T), one, 8, 4096, None)
     assert rc == dl.DLRM_E_SHAPE
 
 
@@ -109,11 +109,11 @@ def test_forward_rejects_missing_or_small_workspace(lib):
     need = lib.dlrm_forward_workspace_bytes(ctypes.byref(m), 16)
     fake = (dl._vp * 3)(4096, 4096, 4096)
     n = dl._i64s([16, 16, 16])
-    assert lib.dlrm_forward(ctypes.byref(m), 16, 4096, fake, n, fake, 4096, None, need, None) == dl.DLRM_E_WORKSPACE
-    assert lib.dlrm_forward(ctypes.byref(m), 16, 4096, fake, n, fake, 4096, 4096, need - 1, None) == dl.DLRM_E_WORKSPACE
-    assert lib.dlrm_forward(ctypes.byref(m), 16, 4096, fake, n, fake, 4096, 4096 + 16, need, None) == dl.DLRM_E_WORKSPACE
-    assert lib.dlrm_forward(None, 16, 4096, fake, n, fake, 4096, 4096, need, None) == dl.DLRM_E_NULL
-    assert lib.dlrm_forward(ctypes.byref(m), 16, None, fake, n, fake, 4096, 4096, need, None) == dl.DLRM_E_NULL
+    assert lib.dlrm_forward(ctypes.byref(m), 16, 4096, fake, n, fake, 8, 4096, None, need, None) == dl.DLRM_E_WORKSPACE
+    assert lib.dlrm_forward(ctypes.byref(m), 16, 4096, fake, n, fake, 8, 4096, 4096, need - 1, None) == dl.DLRM_E_WORKSPACE
+    assert lib.dlrm_forward(ctypes.byref(m), 16, 4096, fake, n, fake, 8, 4096, 4096 + 16, need, None) == dl.DLRM_E_WORKSPACE
+    assert lib.dlrm_forward(None, 16, 4096, fake, n, fake, 8, 4096, 4096, need, None) == dl.DLRM_E_NULL
+    assert lib.dlrm_forward(ctypes.byref(m), 16, None, fake, n, fake, 8, 4096, 4096, need, None) == dl.DLRM_E_NULL
 
 
 def test_layered_forward_rejects_missing_or_small_workspace(lib):
@@ -122,9 +122,9 @@ def test_layered_forward_rejects_missing_or_small_workspace(lib):
     fake = (dl._vp * 3)(4096, 4096, 4096)
     n = dl._i64s([16, 16, 16])
     f = lib.dlrm_forward_layered
-    assert f(ctypes.byref(m), 16, 4096, fake, n, fake, 4096, None, need, None) == dl.DLRM_E_WORKSPACE
-    assert f(ctypes.byref(m), 16, 4096, fake, n, fake, 4096, 4096, need - 1, None) == dl.DLRM_E_WORKSPACE
-    assert f(ctypes.byref(m), 16, 4096, fake, n, fake, 4096, 4096 + 16, need, None) == dl.DLRM_E_WORKSPACE
+    assert f(ctypes.byref(m), 16, 4096, fake, n, fake, 8, 4096, None, need, None) == dl.DLRM_E_WORKSPACE
+    assert f(ctypes.byref(m), 16, 4096, fake, n, fake, 8, 4096, 4096, need - 1, None) == dl.DLRM_E_WORKSPACE
+    assert f(ctypes.byref(m), 16, 4096, fake, n, fake, 8, 4096, 4096 + 16, need, None) == dl.DLRM_E_WORKSPACE
 
 
 @pytest.mark.parametrize("ln_bot,ln_top,T,D,why", [
@@ -139,7 +139,7 @@ def test_fused_forward_rejects_models_outside_its_limits(lib, ln_bot, ln_top, T,
     m, keep = _model(ln_bot, ln_top, T, D)
     fake = (dl._vp * T)(*([4096] * T))
     n = dl._i64s([16] * T)
-    rc = lib.dlrm_forward_fused(ctypes.byref(m), 16, 4096, fake, n, fake, 4096, None)
+    rc = lib.dlrm_forward_fused(ctypes.byref(m), 16, 4096, fake, n, fake, 8, 4096, None)
     assert rc == dl.DLRM_E_UNSUPPORTED, why
 
 
@@ -222,9 +222,9 @@ def test_fused_forward_needs_packed_weights(lib):
     m, keep = _model([13, 8, 16], [22, 8, 1], 3, 16)
     fake = (dl._vp * 3)(4096, 4096, 4096)
     n = dl._i64s([16, 16, 16])
-    assert lib.dlrm_forward_fused(ctypes.byref(m), 16, 4096, fake, n, fake, 4096, None) == dl.DLRM_E_NULL
+    assert lib.dlrm_forward_fused(ctypes.byref(m), 16, 4096, fake, n, fake, 8, 4096, None) == dl.DLRM_E_NULL
     m.packed_w = 4096 + 4
-    assert lib.dlrm_forward_fused(ctypes.byref(m), 16, 4096, fake, n, fake, 4096, None) == dl.DLRM_E_SHAPE
+    assert lib.dlrm_forward_fused(ctypes.byref(m), 16, 4096, fake, n, fake, 8, 4096, None) == dl.DLRM_E_SHAPE
 
 
 def test_fused_forward_argument_errors(lib):
@@ -232,10 +232,10 @@ def test_fused_forward_argument_errors(lib):
     fake = (dl._vp * 3)(4096, 4096, 4096)
     n = dl._i64s([16, 16, 16])
     f = lib.dlrm_forward_fused
-    assert f(None, 16, 4096, fake, n, fake, 4096, None) == dl.DLRM_E_NULL
-    assert f(ctypes.byref(m), 16, None, fake, n, fake, 4096, None) == dl.DLRM_E_NULL
-    assert f(ctypes.byref(m), 16, 4096, fake, n, fake, None, None) == dl.DLRM_E_NULL
-    assert f(ctypes.byref(m), 0, 4096, fake, n, fake, 4096, None) == dl.DLRM_E_SHAPE
+    assert f(None, 16, 4096, fake, n, fake, 8, 4096, None) == dl.DLRM_E_NULL
+    assert f(ctypes.byref(m), 16, None, fake, n, fake, 8, 4096, None) == dl.DLRM_E_NULL
+    assert f(ctypes.byref(m), 16, 4096, fake, n, fake, 8, None, None) == dl.DLRM_E_NULL
+    assert f(ctypes.byref(m), 0, 4096, fake, n, fake, 8, 4096, None) == dl.DLRM_E_SHAPE
 
 
 def test_linear_argument_errors(lib):
@@ -251,14 +251,61 @@ def test_embbag_argument_errors(lib):
     f = lib.dlrm_embbag_sum
     p = (dl._vp * 65)(*([4096] * 65))
     n = dl._i64s([1] * 65)
-    assert f(65, 4, 4, p, n, p, n, p, 4096, None) == dl.DLRM_E_UNSUPPORTED
-    assert f(0, 4, 4, p, n, p, n, p, 4096, None) == dl.DLRM_E_SHAPE
-    assert f(2, 4, 2048, p, n, p, n, p, 4096, None) == dl.DLRM_E_UNSUPPORTED  # dim above 1024
-    assert f(2, 4, 4, p, n, p, n, p, None, None) == dl.DLRM_E_NULL
+    assert f(65, 4, 4, p, n, p, n, p, 8, 4096, None) == dl.DLRM_E_UNSUPPORTED
+    assert f(0, 4, 4, p, n, p, n, p, 8, 4096, None) == dl.DLRM_E_SHAPE
+    assert f(2, 4, 2048, p, n, p, n, p, 8, 4096, None) == dl.DLRM_E_UNSUPPORTED  # dim above 1024
+    assert f(2, 4, 4, p, n, p, n, p, 8, None, None) == dl.DLRM_E_NULL
     z = (dl._vp * 2)(4096, None)
-    assert f(2, 4, 4, z, n, p, n, p, 4096, None) == dl.DLRM_E_NULL
+    assert f(2, 4, 4, z, n, p, n, p, 8, 4096, None) == dl.DLRM_E_NULL
     neg = dl._i64s([1, -1])
-    assert f(2, 4, 4, p, n, p, neg, p, 4096, None) == dl.DLRM_E_SHAPE
+    assert f(2, 4, 4, p, n, p, neg, p, 8, 4096, None) == dl.DLRM_E_SHAPE
+    for width in (0, 2, 16):
+        assert f(2, 4, 4, p, n, p, n, p, width, 4096, None) == dl.DLRM_E_SHAPE   # index width not 4 or 8
+    big = dl._i64s([1 << 31, 1])
+    assert f(2, 4, 4, p, n, p, big, p, 4, 4096, None) == dl.DLRM_E_UNSUPPORTED  # int32 cannot count that far
+
+
+def test_stacked_bag_argument_errors(lib):
+    f = lib.dlrm_embbag_sum_stacked
+    p = (dl._vp * 2)(4096, 4096)
+    n = dl._i64s([4, 4])
+    base = dl._i64s([0, 100])
+    rows = dl._i64s([100, 50])
+    assert f(2, 4, 4, None, base, rows, p, n, p, 8, 4096, None) == dl.DLRM_E_NULL
+    assert f(2, 4, 4, 4096, None, rows, p, n, p, 8, 4096, None) == dl.DLRM_E_NULL
+    assert f(2, 4, 4, 4096, dl._i64s([0, -1]), rows, p, n, p, 8, 4096, None) == dl.DLRM_E_SHAPE
+    assert f(2, 4, 4, 4096, base, dl._i64s([100, 0]), p, n, p, 8, 4096, None) == dl.DLRM_E_SHAPE
+    assert f(2, 4, 4, 4096, base, rows, p, n, p, 3, 4096, None) == dl.DLRM_E_SHAPE
+    assert f(65, 4, 4, 4096, base, rows, p, n, p, 8, 4096, None) == dl.DLRM_E_UNSUPPORTED
+
+
+def test_forward_rejects_other_index_widths(lib):
+    m, keep = _model([13, 8, 4], [10, 8, 1], 3, 4)
+    need = lib.dlrm_forward_workspace_bytes(ctypes.byref(m), 16)
+    fake = (dl._vp * 3)(4096, 4096, 4096)
+    n = dl._i64s([16, 16, 16])
+    for width in (0, 2, 16):
+        assert lib.dlrm_forward(ctypes.byref(m), 16, 4096, fake, n, fake, width, 4096, 4096, need,
+                                None) == dl.DLRM_E_SHAPE
+        assert lib.dlrm_forward_layered(ctypes.byref(m), 16, 4096, fake, n, fake, width, 4096, 4096, need,
+                                        None) == dl.DLRM_E_SHAPE
+        assert lib.dlrm_forward_fused(ctypes.byref(m), 16, 4096, fake, n, fake, width, 4096,
+                                      None) == dl.DLRM_E_SHAPE
+
+
+def test_stacked_model_needs_its_row_bases(lib):
+    """With emb_w NULL the tables come from emb_stacked and emb_row_base."""
+    m, keep = _model([13, 8, 4], [10, 8, 1], 3, 4)
+    need = lib.dlrm_forward_workspace_bytes(ctypes.byref(m), 16)
+    fake = (dl._vp * 3)(4096, 4096, 4096)
+    n = dl._i64s([16, 16, 16])
+    m.emb_w = None
+    assert lib.dlrm_forward(ctypes.byref(m), 16, 4096, fake, n, fake, 8, 4096, 4096, need, None) == dl.DLRM_E_NULL
+    m.emb_stacked = 4096
+    assert lib.dlrm_forward(ctypes.byref(m), 16, 4096, fake, n, fake, 8, 4096, 4096, need, None) == dl.DLRM_E_NULL
+    bad = dl._i64s([0, -5, 10])
+    m.emb_row_base = ctypes.cast(bad, dl._i64p)
+    assert lib.dlrm_forward(ctypes.byref(m), 16, 4096, fake, n, fake, 8, 4096, 4096, need, None) == dl.DLRM_E_SHAPE
 
 
 def test_general_bag_argument_errors(lib):
@@ -289,11 +336,12 @@ def test_fused_bag_interaction_argument_errors(lib):
     f = lib.dlrm_embbag_interact
     p = (dl._vp * 3)(4096, 4096, 4096)
     n = dl._i64s([4, 4, 4])
-    assert f(3, 4, 16, p, n, p, n, p, None, 16, 4096, 22, 1, None) == dl.DLRM_E_NULL
-    assert f(3, 4, 16, p, n, p, n, p, 4096, 8, 4096, 22, 1, None) == dl.DLRM_E_SHAPE
-    assert f(3, 4, 16, p, n, p, n, p, 4096, 16, 4096, 21, 1, None) == dl.DLRM_E_SHAPE
-    assert f(3, 4, 16, p, n, p, n, p, 4096, 16, 4096, 5, 0, None) == dl.DLRM_E_SHAPE
-    assert f(65, 4, 16, p, n, p, n, p, 4096, 16, 4096, 4096, 0, None) == dl.DLRM_E_UNSUPPORTED
+    assert f(3, 4, 16, p, n, p, n, p, 8, None, 16, 4096, 22, 1, None) == dl.DLRM_E_NULL
+    assert f(3, 4, 16, p, n, p, n, p, 8, 4096, 8, 4096, 22, 1, None) == dl.DLRM_E_SHAPE
+    assert f(3, 4, 16, p, n, p, n, p, 8, 4096, 16, 4096, 21, 1, None) == dl.DLRM_E_SHAPE
+    assert f(3, 4, 16, p, n, p, n, p, 8, 4096, 16, 4096, 5, 0, None) == dl.DLRM_E_SHAPE
+    assert f(65, 4, 16, p, n, p, n, p, 8, 4096, 16, 4096, 4096, 0, None) == dl.DLRM_E_UNSUPPORTED
+    assert f(3, 4, 16, p, n, p, n, p, 5, 4096, 16, 4096, 22, 1, None) == dl.DLRM_E_SHAPE    # index width
 
 
 def test_pair_map_and_check_argument_errors(lib):
@@ -301,5 +349,18 @@ def test_pair_map_and_check_argument_errors(lib):
     assert lib.dlrm_pair_index_map(4, None, 4096, None) == dl.DLRM_E_NULL
     p = (dl._vp * 2)(4096, 4096)
     n = dl._i64s([1, 1])
-    assert lib.dlrm_embbag_check_indices(2, 4, n, p, n, p, None, None) == dl.DLRM_E_NULL
-    assert lib.dlrm_embbag_check_indices(0, 4, n, p, n, p, 4096, None) == dl.DLRM_E_SHAPE
+    assert lib.dlrm_embbag_check_indices(2, 4, n, p, n, p, 8, None, None) == dl.DLRM_E_NULL
+    assert lib.dlrm_embbag_check_indices(0, 4, n, p, n, p, 8, 4096, None) == dl.DLRM_E_SHAPE
+    assert lib.dlrm_embbag_check_indices(2, 4, n, p, n, p, 6, 4096, None) == dl.DLRM_E_SHAPE
+
+
+def test_probe_argument_errors(lib):
+    assert lib.dlrm_probe_sink_floats() > 0
+    assert lib.dlrm_probe_read_stream(None, 1024, 4096, None) == dl.DLRM_E_NULL
+    assert lib.dlrm_probe_read_stream(4096, 1022, 4096, None) == dl.DLRM_E_SHAPE     # not a multiple of 4
+    assert lib.dlrm_probe_read_stream(4100, 1024, 4096, None) == dl.DLRM_E_SHAPE     # not 16-byte aligned
+    g = lib.dlrm_probe_gather_rows
+    assert g(None, 100, 64, 4096, 10, 4096, None) == dl.DLRM_E_NULL
+    assert g(4096, 100, 48, 4096, 10, 4096, None) == dl.DLRM_E_SHAPE                # not a power of two
+    assert g(4096, 100, 8, 4096, 10, 4096, None) == dl.DLRM_E_SHAPE
+    assert g(4096, 0, 64, 4096, 10, 4096, None) == dl.DLRM_E_SHAPE
