@@ -102,6 +102,11 @@ def load(build_if_missing: bool = True) -> ctypes.CDLL:
     L.dlrm_forward.argtypes = [ctypes.POINTER(_Model), ctypes.c_int64, _vp, ctypes.POINTER(_vp), _i64p,
                                ctypes.POINTER(_vp), ctypes.c_int32, _vp, _vp, ctypes.c_size_t, _vp]
     L.dlrm_forward_layered.argtypes = L.dlrm_forward.argtypes
+    L.dlrm_forward_noalloc.argtypes = L.dlrm_forward_fused.argtypes = [
+        ctypes.POINTER(_Model), ctypes.c_int64, _vp, ctypes.POINTER(_vp), _i64p, ctypes.POINTER(_vp), ctypes.c_int32,
+        _vp, _vp]
+    L.dlrm_forward_noalloc_max_bytes.argtypes = []
+    L.dlrm_forward_noalloc_max_bytes.restype = ctypes.c_size_t
     L.dlrm_forward_path.argtypes = [ctypes.POINTER(_Model), ctypes.c_int64]
     L.dlrm_forward_path.restype = ctypes.c_int32
     L.dlrm_pack_weights_bytes.argtypes = [ctypes.POINTER(_Model)]
@@ -118,7 +123,8 @@ def load(build_if_missing: bool = True) -> ctypes.CDLL:
     L.dlrm_pair_index_map.argtypes = [ctypes.c_int32, _vp, _vp, _vp]
     for f in ("dlrm_embbag_sum", "dlrm_embbag_sum_stacked", "dlrm_embbag", "dlrm_interact_lower_tri",
               "dlrm_embbag_interact", "dlrm_linear_bias_act", "dlrm_forward", "dlrm_forward_layered",
-              "dlrm_forward_fused", "dlrm_pack_weights", "dlrm_embbag_check_indices", "dlrm_pair_index_map",
+              "dlrm_forward_fused", "dlrm_forward_noalloc", "dlrm_pack_weights", "dlrm_embbag_check_indices",
+              "dlrm_pair_index_map",
               "dlrm_probe_read_stream", "dlrm_probe_gather_rows"):
         getattr(L, f).restype = ctypes.c_int
     if L.dlrm_abi_version() != ABI_VERSION:
@@ -369,7 +375,8 @@ def linear_bias_act(x: torch.Tensor, W: torch.Tensor, bias: Optional[torch.Tenso
     return out
 
 
-FORWARD_PATHS = {"auto": "dlrm_forward", "fused": "dlrm_forward_fused", "layered": "dlrm_forward_layered"}
+FORWARD_PATHS = {"auto": "dlrm_forward", "fused": "dlrm_forward_fused", "layered": "dlrm_forward_layered",
+                 "noalloc": "dlrm_forward_noalloc"}
 
 
 class Model:
@@ -478,7 +485,9 @@ class Model:
                 out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
                 args=None, path: str = "auto") -> torch.Tensor:
         """The whole forward.  ``path``: "auto" (dlrm_forward: the library picks),
-        "fused" (dlrm_forward_fused, one launch) or "layered" (dlrm_forward_layered)."""
+        "fused" (dlrm_forward_fused, one launch), "layered" (dlrm_forward_layered)
+        or "noalloc" (dlrm_forward_noalloc: dlrm_forward with the library's
+        static workspace instead of one passed in)."""
         if path not in FORWARD_PATHS:
             raise ValueError(f"path must be one of {sorted(FORWARD_PATHS)}")
         L = load()
@@ -497,10 +506,11 @@ class Model:
         if args is None:
             args = self.forward_args(dense, indices, offsets)
         b, dp, ip, nn_, op, ib = args
-        if path == "fused":
-            rc = L.dlrm_forward_fused(ctypes.byref(self._desc), b, dp, ip, nn_, op, ib, out.data_ptr(),
-                                      _stream(self.device))
-            _check(rc, "dlrm_forward_fused")
+        if path in ("fused", "noalloc"):
+            fn = FORWARD_PATHS[path]
+            rc = getattr(L, fn)(ctypes.byref(self._desc), b, dp, ip, nn_, op, ib, out.data_ptr(),
+                                _stream(self.device))
+            _check(rc, fn)
             return out
         ws = workspace if workspace is not None else self.workspace(B)
         fn = FORWARD_PATHS[path]

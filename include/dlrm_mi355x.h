@@ -315,6 +315,25 @@ dlrm_status_t dlrm_forward(const dlrm_model_t* m, int64_t batch, const float* de
                            void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * dlrm_forward_noalloc -- dlrm_forward for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments, result and path choice as dlrm_forward
+ * without the workspace: the workspace is a file-scope device array of the
+ * library, dlrm_forward_noalloc_max_bytes() bytes (64 MiB) on each GPU it runs
+ * on, held until the process ends.  Returns DLRM_E_UNSUPPORTED, enqueuing
+ * nothing, when dlrm_forward_workspace_bytes(m, batch) exceeds that size;
+ * DLRM_E_HIP if the array's address on the current device cannot be found.
+ * The call itself allocates and frees nothing.  All calls on one GPU share its
+ * array: calls that overlap in time on one GPU (other streams, other host
+ * threads) race on it; calls in order on one stream are safe.
+ */
+size_t dlrm_forward_noalloc_max_bytes(void);
+dlrm_status_t dlrm_forward_noalloc(const dlrm_model_t* m, int64_t batch, const float* dense,
+                                   const void* const* indices, const int64_t* n_indices,
+                                   const void* const* offsets, int32_t index_bytes, float* out,
+                                   void* stream);
+
+/*
  * dlrm_forward_path -- which path dlrm_forward takes for model m and `batch`
  * samples: DLRM_PATH_FUSED (one launch), DLRM_PATH_LAYERED, or 0 when m or
  * batch is invalid.  Host only.

@@ -364,3 +364,20 @@ def test_probe_argument_errors(lib):
     assert g(4096, 100, 48, 4096, 10, 4096, None) == dl.DLRM_E_SHAPE                # not a power of two
     assert g(4096, 100, 8, 4096, 10, 4096, None) == dl.DLRM_E_SHAPE
     assert g(4096, 0, 64, 4096, 10, 4096, None) == dl.DLRM_E_SHAPE
+
+
+def test_noalloc_forward_checks_before_any_launch(lib):
+    """Invalid models give dlrm_forward's own error codes; a workspace beyond the
+    static array is refused; neither touches the device."""
+    assert lib.dlrm_forward_noalloc_max_bytes() == 64 << 20
+    fake = (dl._vp * 3)(4096, 4096, 4096)
+    n = dl._i64s([16, 16, 16])
+    bad, keep = _model([13, 8, 5], [10, 8, 1], 3, 4)
+    f = lib.dlrm_forward_noalloc
+    assert f(ctypes.byref(bad), 16, 4096, fake, n, fake, 8, 4096, None) == dl.DLRM_E_SHAPE
+    assert f(None, 16, 4096, fake, n, fake, 8, 4096, None) == dl.DLRM_E_NULL
+    big, keep2 = _model([13, 512, 256, 128], [479, 1024, 1024, 512, 256, 1], 26, 128)
+    assert lib.dlrm_forward_workspace_bytes(ctypes.byref(big), 65536) > (64 << 20)
+    fake26 = (dl._vp * 26)(*([4096] * 26))
+    n26 = dl._i64s([65536 * 20] * 26)
+    assert f(ctypes.byref(big), 65536, 4096, fake26, n26, fake26, 8, 4096, None) == dl.DLRM_E_UNSUPPORTED
