@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(HERE, "libdlrm_mi355x.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 SOURCES = ("api.hip", "embbag_interact.hip", "embbag_ex.hip", "gemm.hip", "fused_forward.hip", "hbm_probe.hip",
-           "noalloc.hip")
+           "noalloc.hip", "gram_interact.hip")
 ARCH = "gfx950"
 
 

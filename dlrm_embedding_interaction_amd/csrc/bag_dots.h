@@ -15,7 +15,6 @@
 
 namespace dlrm {
 
-typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 // Explicit LDS accesses for pointers into a dynamic LDS array: the casts make
@@ -27,23 +26,26 @@ __device__ __forceinline__ floatx4 lds_load4(const float* p) { return *(const ld
 __device__ __forceinline__ float lds_load(const float* p) { return *(const lds_float*)p; }
 __device__ __forceinline__ void lds_store4(float* p, floatx4 v) { *(lds_floatx4*)(lds_float*)p = v; }
 __device__ __forceinline__ void lds_store(float* p, float v) { *(lds_float*)p = v; }
+typedef __attribute__((address_space(3))) int64_t lds_int64;
+__device__ __forceinline__ int64_t lds_load8(const int64_t* p) { return *(const lds_int64*)p; }
+__device__ __forceinline__ void lds_store8(int64_t* p, int64_t v) { *(lds_int64*)p = v; }
 
 
 // Sum U bags per lane group.  Bag q[u] (-1 = none) is local bag number
 // q = sl * T + t of sample b_base + sl.  Lane lg of the group owns elements
 // (c * G + lg) * VEC .. + VEC-1 of the row for c < C.  Rows of one bag are
-// added in increasing k, R of them fetched per step.
-template <int VEC, int G, int C, int U, int R>
-__device__ __forceinline__ void gather_bags(const TableArgs& ta, int T, int D, int64_t B, int64_t b_base,
-                                            const int (&q)[U], int lg,
-                                            typename Vec<VEC>::T (&acc)[U][C]) {
+// added in increasing k, R of them fetched per step.  IT is the type of the
+// indices and offsets (see gather_bags below).
+template <int VEC, int G, int C, int U, int R, typename IT>
+__device__ __forceinline__ void gather_bags_t(const TableArgs& ta, int T, int D, int64_t B, int64_t b_base,
+                                              const int (&q)[U], int lg,
+                                              typename Vec<VEC>::T (&acc)[U][C]) {
     using V = Vec<VEC>;
     const float* wp[U];
     const void* ip[U];
     int64_t ks[U];
     int len[U];
     int maxlen = 0;
-    const int i32 = ta.idx32;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         len[u] = 0;
@@ -55,8 +57,8 @@ __device__ __forceinline__ void gather_bags(const TableArgs& ta, int T, int D, i
             const int t = q[u] - sl * T;
             const int64_t b = b_base + sl;
             const void* off = ta.off[t];
-            const int64_t s = ld_index(off, b, i32);
-            const int64_t e = (b + 1 < B) ? ld_index(off, b + 1, i32) : ta.nidx[t];
+            const int64_t s = ld_idx<IT>(off, b);
+            const int64_t e = (b + 1 < B) ? ld_idx<IT>(off, b + 1) : ta.nidx[t];
             len[u] = (int)(e - s);
             wp[u] = ta.w[t];
             ip[u] = ta.idx[t];
@@ -71,7 +73,7 @@ __device__ __forceinline__ void gather_bags(const TableArgs& ta, int T, int D, i
 #pragma unroll
         for (int rr = 0; rr < R; ++rr)
 #pragma unroll
-            for (int u = 0; u < U; ++u) row[rr][u] = (r0 + rr < len[u]) ? ld_index(ip[u], ks[u] + r0 + rr, i32) : -1;
+            for (int u = 0; u < U; ++u) row[rr][u] = (r0 + rr < len[u]) ? ld_idx<IT>(ip[u], ks[u] + r0 + rr) : -1;
         typename V::T v[R][U][C];
 #pragma unroll
         for (int rr = 0; rr < R; ++rr)
@@ -80,7 +82,7 @@ __device__ __forceinline__ void gather_bags(const TableArgs& ta, int T, int D, i
 #pragma unroll
                 for (int c = 0; c < C; ++c) {
                     const int e = (c * G + lg) * VEC;
-                    v[rr][u][c] = (row[rr][u] >= 0 && e < D) ? V::load(wp[u] + row[rr][u] * D + e) : V::zero();
+                    v[rr][u][c] = (row[rr][u] >= 0 && e < D) ? V::gload(wp[u] + row[rr][u] * D + e) : V::zero();
                 }
 #pragma unroll
         for (int rr = 0; rr < R; ++rr)
@@ -91,6 +93,17 @@ __device__ __forceinline__ void gather_bags(const TableArgs& ta, int T, int D, i
                     for (int c = 0; c < C; ++c) acc[u][c] = V::add(acc[u][c], v[rr][u][c]);
                 }
     }
+}
+
+// gather_bags_t with the index type of the launch (one test, the same for
+// every lane, around the whole gather).
+template <int VEC, int G, int C, int U, int R>
+__device__ __forceinline__ void gather_bags(const TableArgs& ta, int T, int D, int64_t B, int64_t b_base,
+                                            const int (&q)[U], int lg, typename Vec<VEC>::T (&acc)[U][C]) {
+    if (ta.idx32)
+        gather_bags_t<VEC, G, C, U, R, int32_t>(ta, T, D, B, b_base, q, lg, acc);
+    else
+        gather_bags_t<VEC, G, C, U, R, int64_t>(ta, T, D, B, b_base, q, lg, acc);
 }
 
 // Z[s * ldz + p] = <S_s[i], S_s[j]> for s < nb and p < P = F(F-1)/2, where

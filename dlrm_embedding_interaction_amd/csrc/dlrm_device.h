@@ -24,11 +24,30 @@ struct TableArgs {
     int idx32;
 };
 
-// Element k of an index or offset array of the launch's width (a branch on a
-// kernel argument, the same for every lane).
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+// A load through a pointer into global memory that the compiler cannot place
+// by itself (pointers kept in per-lane-indexed kernel-argument arrays or in
+// LDS): the cast makes it a global load, counted by vmcnt alone.  Through a
+// generic pointer it would be a flat load, which the compiler must also wait
+// for before every later LDS access.
+template <typename T>
+__device__ __forceinline__ T ld_global(const void* p) {
+    return *(const __attribute__((address_space(1))) T*)p;
+}
+
+// Element k of an index or offset array of element type IT.  The hot loops
+// take IT as a template argument, chosen once per phase: a width test at
+// every load splits the loads into separate blocks, and the compiler then
+// waits for each one before the next is issued.
+template <typename IT>
+__device__ __forceinline__ int64_t ld_idx(const void* base, int64_t k) {
+    return (int64_t)ld_global<IT>(static_cast<const IT*>(base) + k);
+}
+// The same with the width a runtime value (off the hot loops).
 __device__ __forceinline__ int64_t ld_index(const void* base, int64_t k, int idx32) {
-    if (idx32) return (int64_t) static_cast<const int32_t*>(base)[k];
-    return static_cast<const int64_t*>(base)[k];
+    if (idx32) return ld_idx<int32_t>(base, k);
+    return ld_idx<int64_t>(base, k);
 }
 
 // ---- lane-group sums ---------------------------------------------------------

@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "dlrm_device.h"
 
 namespace dlrm {
@@ -22,6 +24,25 @@ constexpr int kFusedSamples = 8;
 constexpr int kMfmaDotsMinTables = 24;           // single launch: MFMA dots for this many tables up to 32
 constexpr int kFusedThreads = 512;
 constexpr size_t kFusedMaxLds = 160 * 1024;
+
+// A kernel's dynamic-LDS limit is raised to the whole 160 KiB once per kernel
+// and device, by whichever thread launches it there first (std::call_once:
+// concurrent first launches wait for that one call).
+template <typename Kernel>
+hipError_t allow_full_lds(Kernel* k) {
+    constexpr int kMaxDevices = 64;
+    static std::once_flag once[kMaxDevices];
+    static hipError_t result[kMaxDevices];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    auto set = [&] {
+        return hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kFusedMaxLds);
+    };
+    if (dev < 0 || dev >= kMaxDevices) return set();
+    std::call_once(once[dev], [&] { result[dev] = set(); });
+    return result[dev];
+}
 
 // One MLP of the single-launch forward: layer l maps dim[l] -> dim[l + 1]
 // with packed weights w[l] (pack_layer_kernel layout) and bias b[l].
@@ -83,6 +104,13 @@ hipError_t launch_embbag_sum(const TableArgs& ta, int T, int D, int64_t B, bool 
 hipError_t launch_interact(const TableArgs* ta, const float* emb, int T, int D, int64_t B, bool aligned16,
                            bool multi_hot, const float* x, int64_t ld_x, float* out, int64_t ld_out, int col_x,
                            int col_z, hipStream_t s);
+
+// Bags of one index and the interaction as a Gram matrix on the matrix cores,
+// for up to 32 tables and rows of 32, 64 or 128 floats (16-byte aligned
+// tables and x); Z to out[:, col_z:col_z+P], x to out[:, col_x:] when col_x >= 0.
+bool gram_interact_supported(int T, int D, bool aligned16);
+hipError_t launch_gram_interact(const TableArgs& ta, int T, int D, int64_t B, bool aligned16, const float* x,
+                                int64_t ld_x, float* out, int64_t ld_out, int col_x, int col_z, hipStream_t s);
 
 // General bags (mode, weights, include_last_offset, padding) into out (B, T, D).
 hipError_t launch_embbag_ex(const BagArgs& ba, int T, int D, int64_t B, int mode, int last_off, bool idx32,

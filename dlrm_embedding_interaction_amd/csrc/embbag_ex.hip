@@ -55,8 +55,8 @@ __global__ __launch_bounds__(kBlock) void embbag_ex_kernel(BagArgs ba, int T, in
             const int64_t b = q[u] / T;
             const int t = (int)(q[u] - b * T);
             const IDX* off = reinterpret_cast<const IDX*>(ba.off[t]);
-            const int64_t s = (int64_t)off[b];
-            const int64_t e = last_off ? (int64_t)off[b + 1] : ((b + 1 < B) ? (int64_t)off[b + 1] : ba.nidx[t]);
+            const int64_t s = ld_idx<IDX>(off, b);
+            const int64_t e = last_off ? ld_idx<IDX>(off, b + 1) : ((b + 1 < B) ? ld_idx<IDX>(off, b + 1) : ba.nidx[t]);
             len[u] = (int)(e - s);
             wp[u] = ba.w[t];
             ip[u] = reinterpret_cast<const IDX*>(ba.idx[t]) + s;
@@ -75,9 +75,9 @@ __global__ __launch_bounds__(kBlock) void embbag_ex_kernel(BagArgs ba, int T, in
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const bool in = r0 + rr < len[u];
-                const int64_t r = in ? (int64_t)ip[u][r0 + rr] : -1;
+                const int64_t r = in ? ld_idx<IDX>(ip[u], r0 + rr) : -1;
                 row[rr][u] = (r == pad[u]) ? -1 : r;     // padding rows leave the bag
-                wt[rr][u] = (in && ps[u]) ? ps[u][r0 + rr] : 1.f;
+                wt[rr][u] = (in && ps[u]) ? ld_global<float>(ps[u] + r0 + rr) : 1.f;
             }
         typename V::T v[R][U][C];
 #pragma unroll
@@ -87,7 +87,7 @@ __global__ __launch_bounds__(kBlock) void embbag_ex_kernel(BagArgs ba, int T, in
 #pragma unroll
                 for (int c = 0; c < C; ++c) {
                     const int e = (c * G + lg) * VEC;
-                    v[rr][u][c] = (row[rr][u] >= 0 && e < D) ? V::load(wp[u] + row[rr][u] * D + e) : V::zero();
+                    v[rr][u][c] = (row[rr][u] >= 0 && e < D) ? V::gload(wp[u] + row[rr][u] * D + e) : V::zero();
                 }
 #pragma unroll
         for (int rr = 0; rr < R; ++rr)

@@ -25,8 +25,6 @@
 //
 // Samples are independent, so blocks never communicate; the weights of one
 // forward (a few MB) stay resident in every XCD's L2.
-#include <mutex>
-
 #include "dlrm_device.h"
 #include "dlrm_internal.h"
 #include "rowvec.h"
@@ -439,25 +437,6 @@ hipError_t launch_pack_small(const SmallBlock& sb, float* dst, hipStream_t s) {
     hipLaunchKernelGGL(pack_small_kernel, dim3((unsigned)((sb.total + kBlock - 1) / kBlock)), dim3(kBlock), 0, s, sb,
                        dst);
     return hipGetLastError();
-}
-
-// The kernel's LDS limit is raised to the whole 160 KiB once per kernel
-// instantiation and device, by whichever thread launches it there first
-// (std::call_once: concurrent first launches wait for that one call).
-template <typename Kernel>
-static hipError_t allow_full_lds(Kernel* k) {
-    constexpr int kMaxDevices = 64;
-    static std::once_flag once[kMaxDevices];
-    static hipError_t result[kMaxDevices];
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    auto set = [&] {
-        return hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kFusedMaxLds);
-    };
-    if (dev < 0 || dev >= kMaxDevices) return set();
-    std::call_once(once[dev], [&] { result[dev] = set(); });
-    return result[dev];
 }
 
 template <int S, int G, int U, int R, int RT>

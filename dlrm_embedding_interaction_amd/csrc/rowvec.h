@@ -12,6 +12,11 @@ template <> struct Vec<4> {
     using T = float4;
     static __device__ __forceinline__ T zero() { return make_float4(0.f, 0.f, 0.f, 0.f); }
     static __device__ __forceinline__ T load(const float* p) { return *reinterpret_cast<const float4*>(p); }
+    // a row of a table or of x in global memory (see ld_global)
+    static __device__ __forceinline__ T gload(const float* p) {
+        const floatx4 v = ld_global<floatx4>(p);
+        return make_float4(v[0], v[1], v[2], v[3]);
+    }
     static __device__ __forceinline__ void store(float* p, T v) { *reinterpret_cast<float4*>(p) = v; }
     static __device__ __forceinline__ T add(T a, T b) { return f4_add(a, b); }
     static __device__ __forceinline__ float dot(T a, T b, float acc) { return f4_dot(a, b, acc); }
@@ -28,6 +33,7 @@ template <> struct Vec<1> {
     using T = float;
     static __device__ __forceinline__ T zero() { return 0.f; }
     static __device__ __forceinline__ T load(const float* p) { return *p; }
+    static __device__ __forceinline__ T gload(const float* p) { return ld_global<float>(p); }
     static __device__ __forceinline__ void store(float* p, T v) { *p = v; }
     static __device__ __forceinline__ T add(T a, T b) { return a + b; }
     static __device__ __forceinline__ float dot(T a, T b, float acc) { return fmaf(a, b, acc); }

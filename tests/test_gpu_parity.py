@@ -694,3 +694,87 @@ def test_forward_at_the_size_limits(T, D, orc):
     w = di.custom(f"limits_{T}_{D}", 64, 5, T, 300, D, 1, (5, 16, D), hidden_top=(32,), cfg_id=20)
     inp = di.make_inputs(w)
     _forward_check(inp, on_gpu(inp), orc)
+
+
+# --- bags + interaction as a Gram matrix on the matrix cores (one-index bags) -----
+
+
+def _int_bags_case(T, D, B, seed, ragged=False, V=300):
+    gen = torch.Generator().manual_seed(seed)
+    tables, idx, off = [], [], []
+    for t in range(T):
+        tables.append(torch.randint(-8, 9, (V, D), generator=gen).float())
+        if ragged and t % 3 == 1:
+            o, n = di.ragged_bags(B, 3, seed * 100 + t, empty_frac=0.3)
+        elif ragged and t % 3 == 2:
+            # one index per bag except a few empty bags
+            lens = torch.ones(B, dtype=torch.int64)
+            lens[torch.rand(B, generator=gen) < 0.1] = 0
+            o = torch.zeros(B, dtype=torch.int64)
+            o[1:] = torch.cumsum(lens[:-1], 0)
+            n = int(lens.sum())
+        else:
+            o, n = torch.arange(B, dtype=torch.int64), B
+        idx.append(torch.randint(0, V, (n,), generator=gen))
+        off.append(o)
+    x = torch.randint(-8, 9, (B, D), generator=gen).float()
+    return tables, idx, off, x
+
+
+@pytest.mark.parametrize("T,D,B", [
+    # one 16x16 tile (F <= 16), then one tile plus the 17th feature, three tiles, three plus the 33rd
+    (1, 64, 4100), (4, 64, 4100), (8, 64, 4100), (15, 64, 4100), (16, 64, 4100), (17, 64, 4100),
+    (24, 64, 4100), (31, 64, 4100), (32, 64, 4100),
+    # rows of 32 and 128 floats
+    (8, 32, 3000), (16, 32, 3000), (32, 32, 3000), (8, 128, 3000), (16, 128, 3000), (20, 128, 3000),
+    (32, 128, 3000),
+    # samples per wave 1, 4 and 8, each with a partly filled last wave
+    (32, 64, 37), (32, 64, 9001), (32, 64, 16500), (8, 64, 20003),
+])
+@pytest.mark.parametrize("itype", [torch.int64, torch.int32])
+def test_gram_interaction_integer_bitexact(T, D, B, itype, orc):
+    """Integer tables and x: every bag sum and dot is exact in fp32, so the Gram
+    kernel must equal the oracle bit for bit, x columns included."""
+    tables, idx, off, x = _int_bags_case(T, D, B, seed=T * 131 + D + B)
+    log(f"gram T={T} D={D} B={B} {itype}")
+    out = dl.embbag_interact([t.cuda() for t in tables], [i.to(itype).cuda() for i in idx],
+                             [o.to(itype).cuda() for o in off], x.cuda(), concat_dense=True)
+    torch.cuda.synchronize()
+    E = orc.embbag_sum(tables, idx, off)
+    Z = orc.interact(x.double().numpy(), E)
+    assert np.array_equal(out.cpu().double().numpy(), np.concatenate([x.double().numpy(), Z], 1))
+
+
+@pytest.mark.parametrize("T,D,B", [(8, 64, 3001), (16, 64, 700), (32, 64, 5000), (32, 128, 1100)])
+def test_gram_interaction_ragged_bags_bitexact(T, D, B, orc):
+    """Empty bags on the fast path, and bags of 2-3 indices that send their waves
+    down the general path; Z written beside x in one buffer, as the forward does."""
+    tables, idx, off, x = _int_bags_case(T, D, B, seed=7 * T + D, ragged=True)
+    P = (T + 1) * T // 2
+    ld = (D + P + 3) // 4 * 4 + 4
+    R = torch.full((B, ld), 99.0)
+    R[:, :D] = x
+    Rg = R.cuda()
+    dl.embbag_interact([t.cuda() for t in tables], [i.cuda() for i in idx], [o.cuda() for o in off], Rg,
+                       concat_dense=False, out=Rg[:, D:])
+    torch.cuda.synchronize()
+    Rc = Rg.cpu()
+    E = orc.embbag_sum(tables, idx, off)
+    Z = orc.interact(x.double().numpy(), E)
+    assert torch.equal(Rc[:, :D], x) and torch.all(Rc[:, D + P:] == 99.0)
+    assert np.array_equal(Rc[:, D:D + P].double().numpy(), Z)
+
+
+@pytest.mark.parametrize("T,D", [(8, 64), (16, 64), (32, 64), (26, 128)])
+def test_gram_interaction_float_within_bound(T, D, orc):
+    """Random fp32 tables and x at batch 8192: every dot within gamma_D sum |u_d v_d|."""
+    B = 8192
+    w = di.custom(f"gramf_{T}_{D}", B, 3, T, 5000, D, 1, (3, D), cfg_id=27)
+    inp = di.make_inputs(w)
+    g = on_gpu(inp)
+    x = torch.randn((B, D), generator=torch.Generator().manual_seed(T))
+    out = dl.embbag_interact(g.tables, g.indices, g.offsets, x.cuda(), concat_dense=False).cpu().double().numpy()
+    E = orc.embbag_sum(inp.tables, inp.indices, inp.offsets)
+    Z = orc.interact(x.double().numpy(), E)
+    mag = orc.interact(x.abs().double().numpy(), np.abs(E))
+    assert np.all(np.abs(out - Z) <= gamma(D) * mag + 1e-30)
