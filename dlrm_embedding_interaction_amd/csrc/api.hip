@@ -353,10 +353,10 @@ bool model_fits_fused(const dlrm_model_t* m) {
 // across the whole chip.  Measured on MI355X over the batch x tables sweep
 // of the 13-512-256-64 / (64+P)-512-256-1 model (both paths replayed from
 // graphs of 8 steps): the single launch is faster up to batch 8192 with up
-// to 16 tables; with 32 tables only from 256 to 4096 when the dots run as one
-// MFMA tile per sample (else from 1024 to 2048), since below that gathering
-// 32 bags and streaming the 592-wide first top layer per block cost more
-// than the layered path's launches.
+// to 16 tables, and up to 4096 with 24 to 32 tables when its dots run as one
+// MFMA tile per sample (otherwise only from 1024 to 2048); past that the
+// layered path, whose bag + interaction kernel forms the dots as a Gram
+// matrix on the matrix cores, wins.
 constexpr int64_t kFusedAutoMaxBatch = 8192;
 constexpr int64_t kFusedAutoMaxWeightBytes = 3 << 20;
 bool fused_preferred(const dlrm_model_t* m, int64_t batch) {
@@ -364,7 +364,7 @@ bool fused_preferred(const dlrm_model_t* m, int64_t batch) {
     if (m->num_tables >= 24) {
         // one MFMA tile per sample takes the dots up to 32 tables (D % 16 == 0)
         const bool gram = m->num_tables <= 32 && m->emb_dim % 16 == 0;
-        return gram ? batch >= 256 && batch <= 4096 : batch >= 1024 && batch <= 2048;
+        return gram ? batch <= 4096 : batch >= 1024 && batch <= 2048;
     }
     return true;
 }

@@ -287,29 +287,16 @@ __global__ __launch_bounds__(kFusedThreads) void fused_forward_kernel(FusedArgs 
     const int64_t b0 = (int64_t)blockIdx.x * S;
     const int nb = (int)min((int64_t)S, fa.B - b0);
 
-    // The L2 of every XCD starts each launch without the weights.  The blocks
-    // of one XCD (the hardware deals blocks to the 8 XCDs round-robin) first
-    // touch every 128-byte line of the packed weights once between them, so
-    // that each layer later streams from L2 rather than from the Infinity
-    // Cache; the touches complete while the bags are gathered.
-    float touch = 0.f;
-    {
-        const int64_t nlines = fa.n_packed >> 5;
-        const int64_t xblocks = max(1u, gridDim.x >> 3);
-        for (int64_t i = (int64_t)(blockIdx.x >> 3) * NT + tid; i < nlines; i += xblocks * NT)
-            touch += fa.packed[i << 5];
-    }
-
-    // 0. zero both activation buffers (reads past a layer's K must be finite)
-    for (int i = tid; i < (2 * S * lda) / 4; i += NT) lds4[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-    __syncthreads();
-
-    // 1. dense rows into buffer 0, the last layer's weights into LDS
+    // 1. dense rows into buffer 0, zeros in its columns [n0, round_up(n0, 64))
+    //    that the first layer's 64-wide k steps read past n0 (every layer
+    //    writes the zeros past its own width, mlp_layer), and in the rows of
+    //    samples past the batch; the last layer's weights into LDS
     const int n0 = fa.bot.dim[0];
-    for (int i = tid; i < nb * n0; i += NT) {
-        const int s = i / n0;
-        const int k = i - s * n0;
-        lds_store(buf(0) + s * lda + k, fa.dense[(b0 + s) * n0 + k]);
+    const int w0 = (n0 + 63) & ~63;
+    for (int i = tid; i < S * w0; i += NT) {
+        const int s = i / w0;
+        const int k = i - s * w0;
+        lds_store(buf(0) + s * lda + k, (s < nb && k < n0) ? fa.dense[(b0 + s) * n0 + k] : 0.f);
     }
     // one contiguous copy, so that no layer waits on a bias load later
     for (int i = tid; i < (fa.n_small >> 2); i += NT)
@@ -401,7 +388,6 @@ __global__ __launch_bounds__(kFusedThreads) void fused_forward_kernel(FusedArgs 
         cur ^= 1;
     }
     last_layer<S>(buf(cur), lda, klast, wlast, lds_load(wlast + ((klast + 3) & ~3)), fa.out + b0, nb);
-    asm volatile("; touched %0" ::"v"(touch));  // keeps the touch loads
 }
 
 // ---- host side ------------------------------------------------------------------

@@ -332,10 +332,13 @@ hipError_t launch_gram_t(const TableArgs& ta, int T, int64_t B, const float* x, 
 template <int D, int NB, bool EXTRA>
 hipError_t launch_gram_ns(const TableArgs& ta, int T, int64_t B, const float* x, int64_t ld_x, float* out,
                           int64_t ld_out, int col_x, int col_z, hipStream_t s) {
-    // samples per wave: so many that every wave is resident at once (256 CUs
-    // x 8 waves) and pays the bag-bound and index round trips only once; at
-    // most 8 samples per wave
-    const int64_t want = (B + 2047) / 2048;
+    // samples per wave: so many that every wave is resident at once and pays
+    // the bag-bound and index round trips only once (256 CUs x 4 SIMDs x the
+    // waves per SIMD the registers allow: about 4 with one 16-feature block,
+    // 2 with more; measured at batch 16384: 8 tables 13.6 -> 12.7 us with 4,
+    // 16 tables 18.4 -> 19.8 us); at most 8 samples per wave
+    constexpr int64_t kResidentWaves = 1024 * (NB == 1 && !EXTRA ? 4 : 2);
+    const int64_t want = (B + kResidentWaves - 1) / kResidentWaves;
     if (want <= 1) return launch_gram_t<D, NB, EXTRA, 1>(ta, T, B, x, ld_x, out, ld_out, col_x, col_z, s);
     if (want <= 2) return launch_gram_t<D, NB, EXTRA, 2>(ta, T, B, x, ld_x, out, ld_out, col_x, col_z, s);
     if (want <= 4) return launch_gram_t<D, NB, EXTRA, 4>(ta, T, B, x, ld_x, out, ld_out, col_x, col_z, s);

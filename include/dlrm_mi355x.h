@@ -302,8 +302,8 @@ size_t dlrm_forward_workspace_bytes(const dlrm_model_t* m, int64_t batch);
  * Enqueues either one kernel (the single-launch path of dlrm_forward_fused,
  * taken when m->packed_w is set, the model fits that path, its Linear weights
  * take at most 3 MiB and the batch is where it measured faster: at most 8192
- * with fewer than 24 tables, 256..4096 with 24 to 32 tables and a row length
- * that is a multiple of 16, 1024..2048 otherwise) or a few kernels
+ * with fewer than 24 tables, at most 4096 with 24 to 32 tables and a row
+ * length that is a multiple of 16, 1024..2048 otherwise) or a few kernels
  * (dlrm_forward_layered) on `stream`; the
  * workspace must not be used by another call until they finish.  Both paths
  * compute the same function;

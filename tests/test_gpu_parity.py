@@ -422,7 +422,7 @@ def test_forward_zero_last_layer_gives_exactly_half(path):
 def test_forward_auto_path_choice():
     """dlrm_forward takes the single launch for the page-4 model, and the layered
     path once the weights no longer fit in L2 (here 4 MB in one top layer), past
-    batch 8192, for 32 tables below batch 512, or without packed weights."""
+    batch 8192, for 32 tables past batch 4096, or without packed weights."""
     g = on_gpu(di.make_inputs(di.PAGE4))
     m = dl.Model.from_inputs(g)
     auto = m.forward(g.dense, g.indices, g.offsets).clone()
@@ -434,7 +434,7 @@ def test_forward_auto_path_choice():
         unpacked.forward(g.dense, g.indices, g.offsets, path="fused")
     assert e.value.code == dl.DLRM_E_NULL
     cases = [di.custom("big_top", 96, 13, 3, 1000, 64, 1, (13, 64), hidden_top=(1024, 1024), cfg_id=23),
-             di.sweep(16384, 1), di.sweep(128, 32)]
+             di.sweep(16384, 1), di.sweep(8192, 32)]
     for w in cases:
         g = on_gpu(di.make_inputs(w))
         m = dl.Model.from_inputs(g)

@@ -184,7 +184,7 @@ def test_pack_weights_argument_errors(lib):
 
 def test_forward_path_choice(lib):
     """Layered without packed weights; with them the single launch up to batch
-    8192 (256..4096 with 24-32 tables and rows a multiple of 16, 1024..2048
+    8192 (up to 4096 with 24-32 tables and rows a multiple of 16, 1024..2048
     with more tables); 0 for invalid input.  Host only."""
     m, keep = _model([13, 512, 256, 64], [70, 512, 256, 1], 3, 64)
     assert lib.dlrm_forward_path(ctypes.byref(m), 2048) == 1
@@ -202,7 +202,8 @@ def test_forward_path_choice(lib):
     assert lib.dlrm_forward_path(ctypes.byref(m16), 8193) == 1
     m32, keep32 = _model([13, 512, 256, 64], [64 + 528, 512, 256, 1], 32, 64)
     m32.packed_w = 4096
-    assert lib.dlrm_forward_path(ctypes.byref(m32), 128) == 1
+    assert lib.dlrm_forward_path(ctypes.byref(m32), 16) == 2
+    assert lib.dlrm_forward_path(ctypes.byref(m32), 128) == 2
     assert lib.dlrm_forward_path(ctypes.byref(m32), 256) == 2
     assert lib.dlrm_forward_path(ctypes.byref(m32), 512) == 2
     assert lib.dlrm_forward_path(ctypes.byref(m32), 1024) == 2
