@@ -76,7 +76,8 @@ def parse():
     p.add_argument("--sweep", metavar="OUT_JSON", default=None,
                    help="time every batch x tables cell of the sweep grid, write them to OUT_JSON, print no line")
     p.add_argument("--copy-calibration", action="store_true",
-                   help="also run a 512 MiB device copy, the reference kernel for HBM byte counters")
+                   help="also run a 512 MiB read (the library's probe) and a 512 MiB copy, the reference "
+                        "kernels for the HBM byte counters")
     return p.parse_args()
 
 
@@ -137,7 +138,7 @@ def main():
         run_sweep(torch, dl, di, dev, args)
         return
     if args.copy_calibration:
-        copy_calibration(torch, dev)
+        copy_calibration(torch, dl, dev)
     w = di.get(args.workload)
 
     res = run_workload(torch, dl, di, w, dev, args)
@@ -174,11 +175,12 @@ def main():
         "kernels": res["kernels"],
     }
     ceil = None
-    if not args.copy_calibration:   # counter runs keep the calibration copy the only copy kernel
+    if not args.copy_calibration:   # counter runs keep the calibration kernels the only probes
         ceil = ceilings(torch, dl, dev)
         out["ceilings"] = ceil
         re = out["roofline_emb_interact"]
         re["frac_of_read_ceiling"] = re["achieved"] / ceil["read_stream_GBps"]
+        l2_floor(out["roofline"], ceil)
     if not args.no_secondary and w.name != di.MANYTABLE.name:
         w2 = di.MANYTABLE
         r2 = run_workload(torch, dl, di, w2, dev, args)
@@ -189,6 +191,8 @@ def main():
                        "mlp_TFLOPs": r2["mlp_tflops"],
                        "emb_interact_GBps": r2["roofline_emb"]["achieved"],
                        "roofline": r2["roofline"], "roofline_emb_interact": r2["roofline_emb"]}
+        if ceil:
+            l2_floor(out["nc32"]["roofline"], ceil)
     if not args.no_large:
         out["emb_interact_large"] = large_cells(torch, dl, di, dev, args, ceil)
     if not args.no_cpu_baseline:
@@ -446,9 +450,26 @@ def roofline(kernels, dominant=True, traffic=None):
                 "us_per_launch": k["us"], "flops_per_launch": k["flops"],
                 "shape": [k.get("M"), k.get("N"), k.get("K")]}
     achieved = k["bytes"] / sec / 1e9
-    return {"kernel": k["name"], "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBPS, "traffic": tr, "us_per_launch": k["us"],
-            "bytes_per_launch": k["bytes"]}
+    out = {"kernel": k["name"], "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+           "frac": achieved / HBM_PEAK_GBPS, "traffic": tr, "us_per_launch": k["us"],
+           "bytes_per_launch": k["bytes"]}
+    if tr:
+        # counted L2-miss bytes (Infinity Cache hits included) over the same time: with reused rows
+        # (Zipf bags) the algorithmic rate counts every reuse and can pass the peak; this one cannot
+        out["counted_l2_miss_GBps"] = tr / sec / 1e9
+        out["frac_counted_l2_miss"] = tr / sec / 1e9 / HBM_PEAK_GBPS
+    return out
+
+
+def l2_floor(roof, ceil):
+    """For the single-launch kernel: every block streams all packed weights
+    from L2, so one block's weight bytes over the measured per-CU L2 rate is a
+    floor on the kernel's time (one block per CU at batch 2048)."""
+    wb = roof.get("weights_streamed_per_block_bytes")
+    if wb and ceil.get("l2_stream_GBps_per_cu"):
+        fl = wb / (ceil["l2_stream_GBps_per_cu"] * 1e9) * 1e6
+        roof["l2_stream_floor_us"] = fl
+        roof["frac_of_l2_stream_floor"] = fl / roof["us_per_launch"]
 
 
 def _time_graph(torch, f, reps, rounds=3):
@@ -494,10 +515,20 @@ def ceilings(torch, dl, dev, nbytes=2 << 30, gather_rows=1 << 21, dim=64):
     gather = gbytes / (us_g * 1e-6) / 1e9
     del table, idx
     torch.cuda.empty_cache()
+    # L2 -> CU: one block per CU reads the same 1.5 MiB (L2-resident after the
+    # first pass), as the single launch streams its packed weights
+    l2b = 3 << 19
+    l2src = torch.ones(l2b // 4, device=dev)
+    us_l2 = _time_graph(torch, lambda: dl.probe_l2_stream(l2src, blocks=256), reps=20)
+    l2_cu = l2b / (us_l2 * 1e-6) / 1e9
+    del l2src
+    torch.cuda.empty_cache()
     return {"read_stream_GBps": read, "read_stream_frac_of_peak": read / HBM_PEAK_GBPS,
             "read_stream_bytes": nbytes, "gather_rows_GBps": gather,
             "gather_rows_frac_of_peak": gather / HBM_PEAK_GBPS,
-            "gather_rows": gather_rows, "gather_row_bytes": dim * 4, "gather_bytes_incl_int64_index": gbytes}
+            "gather_rows": gather_rows, "gather_row_bytes": dim * 4, "gather_bytes_incl_int64_index": gbytes,
+            "l2_stream_GBps_per_cu": l2_cu, "l2_stream_B_per_clk_per_cu_at_2p4GHz": l2_cu / 2.4,
+            "l2_stream_bytes_per_block": l2b}
 
 
 LARGE_CELLS = ((16384, 8), (16384, 16), (16384, 32))
@@ -527,6 +558,10 @@ def large_cells(torch, dl, di, dev, args, ceil):
         nbytes = B * T * w.bag * (D * 4 + ib) + B * T * ib + B * D * 4 + B * P * 4
         gbps = nbytes / (us * 1e-6) / 1e9
         cell = {"us": us, "bytes": nbytes, "GBps": gbps, "frac_of_peak": gbps / HBM_PEAK_GBPS}
+        tr = counted_traffic(w.name).get("emb_interact") if ib == 8 else None
+        if tr:
+            cell["traffic"] = tr
+            cell["counted_GBps"] = tr / (us * 1e-6) / 1e9
         if ceil:
             cell["frac_of_read_ceiling"] = gbps / ceil["read_stream_GBps"]
             cell["frac_of_gather_ceiling"] = gbps / ceil["gather_rows_GBps"]
@@ -537,15 +572,20 @@ def large_cells(torch, dl, di, dev, args, ceil):
     return out
 
 
-def copy_calibration(torch, dev, nbytes=512 << 20, reps=5):
-    """A plain device-to-device copy of known size: its FETCH_SIZE / WRITE_SIZE per
-    dispatch scale the counters of the measured kernels to bytes."""
+def copy_calibration(torch, dl, dev, nbytes=512 << 20, reps=5):
+    """Kernels of known traffic whose FETCH_SIZE / WRITE_SIZE per dispatch scale
+    the counters of the measured kernels to bytes: the library's read-stream
+    probe over 512 MiB (read once, nothing written) and a 512 MiB device copy
+    (read and written once)."""
     a = torch.ones(nbytes // 4, device=dev)
+    for _ in range(reps):
+        dl.probe_read_stream(a)
     b = torch.empty_like(a)
     for _ in range(reps):
         b.copy_(a)
     torch.cuda.synchronize()
-    print(f"[bench] copy calibration: {reps} copies of {nbytes} bytes", file=sys.stderr, flush=True)
+    print(f"[bench] counter calibration: {reps} reads and {reps} copies of {nbytes} bytes", file=sys.stderr,
+          flush=True)
     del a, b
 
 

@@ -120,12 +120,13 @@ def load(build_if_missing: bool = True) -> ctypes.CDLL:
     L.dlrm_probe_sink_floats.restype = ctypes.c_int64
     L.dlrm_probe_read_stream.argtypes = [_vp, ctypes.c_int64, _vp, _vp]
     L.dlrm_probe_gather_rows.argtypes = [_vp, ctypes.c_int64, ctypes.c_int32, _vp, ctypes.c_int64, _vp, _vp]
+    L.dlrm_probe_l2_stream.argtypes = [_vp, ctypes.c_int64, ctypes.c_int32, _vp, _vp]
     L.dlrm_pair_index_map.argtypes = [ctypes.c_int32, _vp, _vp, _vp]
     for f in ("dlrm_embbag_sum", "dlrm_embbag_sum_stacked", "dlrm_embbag", "dlrm_interact_lower_tri",
               "dlrm_embbag_interact", "dlrm_linear_bias_act", "dlrm_forward", "dlrm_forward_layered",
               "dlrm_forward_fused", "dlrm_forward_noalloc", "dlrm_pack_weights", "dlrm_embbag_check_indices",
               "dlrm_pair_index_map",
-              "dlrm_probe_read_stream", "dlrm_probe_gather_rows"):
+              "dlrm_probe_read_stream", "dlrm_probe_gather_rows", "dlrm_probe_l2_stream"):
         getattr(L, f).restype = ctypes.c_int
     if L.dlrm_abi_version() != ABI_VERSION:
         raise ImportError(f"{LIBRARY}: ABI version {L.dlrm_abi_version()} != {ABI_VERSION}")
@@ -567,4 +568,16 @@ def probe_gather_rows(table: torch.Tensor, idx: torch.Tensor, sink: Optional[tor
         sink = torch.zeros(int(L.dlrm_probe_sink_floats()), dtype=torch.float32, device=table.device)
     _check(L.dlrm_probe_gather_rows(table.data_ptr(), table.shape[0], table.shape[1], idx.data_ptr(), idx.numel(),
                                     sink.data_ptr(), _stream(table.device)), "dlrm_probe_gather_rows")
+    return sink
+
+
+def probe_l2_stream(src: torch.Tensor, blocks: int = 256, sink: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Enqueue `blocks` blocks that each read all of the fp32 CUDA tensor `src`
+    (numel a multiple of 4): one block per CU measures the L2 -> CU rate."""
+    L = load()
+    _dev(src, torch.float32, "src")
+    if sink is None:
+        sink = torch.zeros(int(L.dlrm_probe_sink_floats()), dtype=torch.float32, device=src.device)
+    _check(L.dlrm_probe_l2_stream(src.data_ptr(), src.numel(), int(blocks), sink.data_ptr(), _stream(src.device)),
+           "dlrm_probe_l2_stream")
     return sink

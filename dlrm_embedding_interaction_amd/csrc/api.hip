@@ -560,6 +560,14 @@ DLRM_API dlrm_status_t dlrm_probe_read_stream(const float* src, int64_t n_floats
     return from_hip(launch_read_stream(src, n_floats, sink, (hipStream_t)stream));
 }
 
+DLRM_API dlrm_status_t dlrm_probe_l2_stream(const float* src, int64_t n_floats, int32_t blocks, float* sink,
+                                            void* stream) {
+    if (!src || !sink) return DLRM_E_NULL;
+    if (n_floats < 4 || n_floats % 4 != 0 || blocks < 1 || blocks > 65536) return DLRM_E_SHAPE;
+    if (!al16(src)) return DLRM_E_SHAPE;
+    return from_hip(launch_l2_stream(src, n_floats, blocks, sink, (hipStream_t)stream));
+}
+
 DLRM_API dlrm_status_t dlrm_probe_gather_rows(const float* table, int64_t rows, int32_t dim, const int64_t* idx,
                                               int64_t n, float* sink, void* stream) {
     if (!table || !idx || !sink) return DLRM_E_NULL;

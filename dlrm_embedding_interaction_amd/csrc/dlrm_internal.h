@@ -146,6 +146,7 @@ hipError_t launch_pair_index_map(int F, int32_t* i_out, int32_t* j_out, hipStrea
 // by idx; sink holds probe_blocks() floats and is written only in theory.
 int probe_blocks();
 hipError_t launch_read_stream(const float* src, int64_t n_floats, float* sink, hipStream_t s);
+hipError_t launch_l2_stream(const float* src, int64_t n_floats, int blocks, float* sink, hipStream_t s);
 hipError_t launch_gather_rows(const float* table, int dim, const int64_t* idx, int64_t n, float* sink,
                               hipStream_t s);
 

@@ -423,12 +423,18 @@ dlrm_status_t dlrm_pair_index_map(int32_t n_feat, int32_t* i_out, int32_t* j_out
  *
  * dlrm_probe_read_stream -- reads n_floats (a multiple of 4, src 16-byte
  *   aligned) of device memory once, sequentially, 16 bytes per lane.
+ * dlrm_probe_l2_stream -- `blocks` blocks of 512 threads each read all
+ *   n_floats (a multiple of 4, src 16-byte aligned): with src small enough to
+ *   stay in L2 and one block per CU, the rate at which one CU pulls L2-resident
+ *   data (the single-launch forward streams its packed weights this way).
  * dlrm_probe_gather_rows -- reads the n rows idx[0..n) (int64, each in
  *   [0, rows)) of the (rows, dim) fp32 table, dim in {16, 32, 64, 128, 256},
  *   table 16-byte aligned: the access pattern of one-index bags.
  */
 int64_t dlrm_probe_sink_floats(void);
 dlrm_status_t dlrm_probe_read_stream(const float* src, int64_t n_floats, float* sink, void* stream);
+dlrm_status_t dlrm_probe_l2_stream(const float* src, int64_t n_floats, int32_t blocks, float* sink,
+                                   void* stream);
 dlrm_status_t dlrm_probe_gather_rows(const float* table, int64_t rows, int32_t dim, const int64_t* idx,
                                      int64_t n, float* sink, void* stream);
 

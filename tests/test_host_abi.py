@@ -365,6 +365,10 @@ def test_probe_argument_errors(lib):
     assert g(4096, 100, 48, 4096, 10, 4096, None) == dl.DLRM_E_SHAPE                # not a power of two
     assert g(4096, 100, 8, 4096, 10, 4096, None) == dl.DLRM_E_SHAPE
     assert g(4096, 0, 64, 4096, 10, 4096, None) == dl.DLRM_E_SHAPE
+    l2 = lib.dlrm_probe_l2_stream
+    assert l2(None, 1024, 256, 4096, None) == dl.DLRM_E_NULL
+    assert l2(4096, 1024, 0, 4096, None) == dl.DLRM_E_SHAPE
+    assert l2(4096, 1026, 256, 4096, None) == dl.DLRM_E_SHAPE
 
 
 def test_noalloc_forward_checks_before_any_launch(lib):
