@@ -69,11 +69,14 @@ __device__ __forceinline__ void gather_bags_t(const TableArgs& ta, int T, int D,
         for (int c = 0; c < C; ++c) acc[u][c] = V::zero();
     }
     for (int r0 = 0; r0 < maxlen; r0 += R) {
-        int64_t row[R][U];
+        // kept in the index type until every load of the step is issued: a
+        // widening inside each conditional load would wait for that load
+        IT row[R][U];
 #pragma unroll
         for (int rr = 0; rr < R; ++rr)
 #pragma unroll
-            for (int u = 0; u < U; ++u) row[rr][u] = (r0 + rr < len[u]) ? ld_idx<IT>(ip[u], ks[u] + r0 + rr) : -1;
+            for (int u = 0; u < U; ++u)
+                row[rr][u] = (r0 + rr < len[u]) ? ld_global<IT>((const IT*)ip[u] + ks[u] + r0 + rr) : IT(-1);
         typename V::T v[R][U][C];
 #pragma unroll
         for (int rr = 0; rr < R; ++rr)
@@ -82,7 +85,7 @@ __device__ __forceinline__ void gather_bags_t(const TableArgs& ta, int T, int D,
 #pragma unroll
                 for (int c = 0; c < C; ++c) {
                     const int e = (c * G + lg) * VEC;
-                    v[rr][u][c] = (row[rr][u] >= 0 && e < D) ? V::gload(wp[u] + row[rr][u] * D + e) : V::zero();
+                    v[rr][u][c] = (row[rr][u] >= 0 && e < D) ? V::gload(wp[u] + (int64_t)row[rr][u] * D + e) : V::zero();
                 }
 #pragma unroll
         for (int rr = 0; rr < R; ++rr)

@@ -68,17 +68,24 @@ __global__ __launch_bounds__(kBlock) void embbag_ex_kernel(BagArgs ba, int T, in
         for (int c = 0; c < C; ++c) acc[u][c] = init;
     }
     for (int r0 = 0; r0 < maxlen; r0 += R) {
-        int64_t row[R][U];
+        // indices stay in their own type until every load of the step is
+        // issued: a widening inside each conditional load would wait for it
+        IDX raw[R][U];
         float wt[R][U];
 #pragma unroll
         for (int rr = 0; rr < R; ++rr)
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const bool in = r0 + rr < len[u];
-                const int64_t r = in ? ld_idx<IDX>(ip[u], r0 + rr) : -1;
-                row[rr][u] = (r == pad[u]) ? -1 : r;     // padding rows leave the bag
+                raw[rr][u] = in ? ld_global<IDX>(ip[u] + r0 + rr) : IDX(-1);
                 wt[rr][u] = (in && ps[u]) ? ld_global<float>(ps[u] + r0 + rr) : 1.f;
             }
+        int64_t row[R][U];
+#pragma unroll
+        for (int rr = 0; rr < R; ++rr)
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                row[rr][u] = ((int64_t)raw[rr][u] == pad[u]) ? -1 : (int64_t)raw[rr][u];  // padding rows leave the bag
         typename V::T v[R][U][C];
 #pragma unroll
         for (int rr = 0; rr < R; ++rr)
