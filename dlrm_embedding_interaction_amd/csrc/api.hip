@@ -103,7 +103,7 @@ void make_plan(const dlrm_model_t* m, int64_t B, Plan* p) {
 
 }  // namespace
 
-DLRM_API const char* dlrm_status_string(dlrm_status_t s) {
+DLRM_API const char* dlrm_status_string(int32_t s) {
     switch (s) {
         case DLRM_OK: return "DLRM_OK";
         case DLRM_E_NULL: return "DLRM_E_NULL: a required pointer is NULL";

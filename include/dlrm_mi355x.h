@@ -438,8 +438,10 @@ dlrm_status_t dlrm_probe_l2_stream(const float* src, int64_t n_floats, int32_t b
 dlrm_status_t dlrm_probe_gather_rows(const float* table, int64_t rows, int32_t dim, const int64_t* idx,
                                      int64_t n, float* sink, void* stream);
 
-/* Human-readable name of a status code (static storage). */
-const char* dlrm_status_string(dlrm_status_t status);
+/* Human-readable name of a status code (static storage).  The code is taken
+ * as a plain integer so that any value a caller holds, including ones this
+ * library never returns, is valid input ("unknown dlrm_status_t" for those). */
+const char* dlrm_status_string(int32_t status);
 
 /* ABI version of this header, bumped on any incompatible change. */
 int32_t dlrm_abi_version(void);
