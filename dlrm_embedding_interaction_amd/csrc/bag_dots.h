@@ -41,29 +41,42 @@ __device__ __forceinline__ void gather_bags_t(const TableArgs& ta, int T, int D,
                                               const int (&q)[U], int lg,
                                               typename Vec<VEC>::T (&acc)[U][C]) {
     using V = Vec<VEC>;
+    // Bag bounds in passes over the U slots, every load of a pass in flight
+    // together: first each slot's table pointers (kernel arguments indexed per
+    // lane), then both of its offsets.  No load sits under a per-slot branch:
+    // waiting for a load whose value the same slot needs at once would also
+    // wait for every older load, one slot after the other.  A slot without a
+    // bag reads sample b_base of table 0 (always valid) and gets length 0.
     const float* wp[U];
     const void* ip[U];
+    const IT* op[U];
+    int64_t nid[U];
+    int64_t bb[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int qq = q[u] >= 0 ? q[u] : 0;
+        const int sl = qq / T;
+        const int t = qq - sl * T;
+        bb[u] = b_base + sl;
+        wp[u] = ta.w[t];
+        ip[u] = ta.idx[t];
+        op[u] = static_cast<const IT*>(ta.off[t]);
+        nid[u] = ta.nidx[t];
+    }
+    IT s0[U], e0[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        s0[u] = ld_global<IT>(op[u] + bb[u]);
+        e0[u] = ld_global<IT>(op[u] + (bb[u] + 1 < B ? bb[u] + 1 : bb[u]));
+    }
     int64_t ks[U];
     int len[U];
     int maxlen = 0;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        len[u] = 0;
-        wp[u] = nullptr;
-        ip[u] = nullptr;
-        ks[u] = 0;
-        if (q[u] >= 0) {
-            const int sl = q[u] / T;
-            const int t = q[u] - sl * T;
-            const int64_t b = b_base + sl;
-            const void* off = ta.off[t];
-            const int64_t s = ld_idx<IT>(off, b);
-            const int64_t e = (b + 1 < B) ? ld_idx<IT>(off, b + 1) : ta.nidx[t];
-            len[u] = (int)(e - s);
-            wp[u] = ta.w[t];
-            ip[u] = ta.idx[t];
-            ks[u] = s;
-        }
+        ks[u] = s0[u];
+        const int64_t e = bb[u] + 1 < B ? (int64_t)e0[u] : nid[u];
+        len[u] = q[u] >= 0 ? (int)(e - ks[u]) : 0;
         maxlen = max(maxlen, len[u]);
 #pragma unroll
         for (int c = 0; c < C; ++c) acc[u][c] = V::zero();

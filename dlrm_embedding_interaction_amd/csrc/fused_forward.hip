@@ -54,11 +54,11 @@ __device__ __forceinline__ float dpp_row_ror8(float v) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));
 }
 
-// out[s][c] = 0 for s < S and c in [c0, c1) (all threads of the block).
-template <int S>
+// out[s][c] = 0 for s < S and c in [c0, c1) (threads 0 .. NT-1 of the block).
+template <int S, int NT = kFusedThreads>
 __device__ __forceinline__ void zero_columns(float* out, int ldo, int c0, int c1) {
     const int w = c1 - c0;
-    for (int i = threadIdx.x; i < S * w; i += kFusedThreads) {
+    for (int i = threadIdx.x; i < S * w; i += NT) {
         const int s = i / w;
         lds_store(out + s * ldo + c0 + (i - s * w), 0.f);
     }
@@ -88,18 +88,17 @@ __global__ __launch_bounds__(kBlock) void pack_layer_kernel(const float* __restr
 
 // out[s][n] = act(sum_k in[s][k] W[n][k] + bias[n]) for s < S, n < N, with in,
 // out and bias in LDS (row strides ldi, ldo) and W packed as above.  The N outputs
-// form tiles of 16 features; wave w takes tiles w, w + NW, ... in passes of TW
-// tiles.  One step covers KU chunks of 16 k values; the weights of a step are
+// form tiles of 16 features; wave w (of the NW waves 0 .. NW-1 that run the
+// layer) takes tiles w, w + NW, ... in passes of TW tiles.  One step covers KU chunks of 16 k values; the weights of a step are
 // requested PD steps ahead into a register ring whose slots are fixed at
 // compile time (no register copies, so the wait before a step's MFMAs covers
 // only that step's loads).  Each load of a wave is 1 KiB of contiguous packed
 // weights.  in[s][k] must be zero for k in [K, round_up(K, 64)); on return
 // out[s][n] is zero for n in [N, round_up(N, 64)).
-template <int S, int TW, int KU, int PD>
+template <int S, int TW, int KU, int PD, int NW>
 __device__ __forceinline__ void mlp_layer(const float* in, int ldi, int K, const float* __restrict__ Wp,
                                           const float* bias, int N, bool relu, float* out, int ldo) {
     constexpr int SG = S / 4;
-    constexpr int NW = kFusedThreads / 64;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int e = lane & 3;
@@ -209,7 +208,7 @@ __device__ __forceinline__ void mlp_layer(const float* in, int ldi, int K, const
             }
         }
     }
-    zero_columns<S>(out, ldo, (N + 15) & ~15, (N + 63) & ~63);
+    zero_columns<S, 64 * NW>(out, ldo, (N + 15) & ~15, (N + 63) & ~63);
 }
 
 // Layer dispatch: TW = tiles per wave and pass, KU chunks of 16 k per step and
@@ -219,15 +218,14 @@ __device__ __forceinline__ void mlp_layer(const float* in, int ldi, int K, const
 // up their MFMAs too (8 samples: 512->256 layer 6.9 -> 6.3 us, 256->64 2.6 ->
 // 2.1 us; 16 samples: batch 4096 x 4 tables 44.3 -> 42.5 us per forward);
 // four-tile layers keep 6 steps.
-template <int S>
+template <int S, int NW = kFusedThreads / 64>
 __device__ __forceinline__ void mlp_layer_any(const float* in, int ldi, int K, const float* Wp, const float* bias,
                                               int N, bool relu, float* out, int ldo) {
-    constexpr int NW = kFusedThreads / 64;
     const int ntile = (N + 15) >> 4;
     const int tw = (ntile + NW - 1) / NW;
 #define DLRM_LAYER(TW_, KU_, PD_)                                               \
     {                                                                           \
-        mlp_layer<S, TW_, KU_, PD_>(in, ldi, K, Wp, bias, N, relu, out, ldo);   \
+        mlp_layer<S, TW_, KU_, PD_, NW>(in, ldi, K, Wp, bias, N, relu, out, ldo); \
         return;                                                                 \
     }
     const int nkc = (K + 15) >> 4;
@@ -263,7 +261,31 @@ __device__ __forceinline__ void last_layer(const float* in, int ldi, int K, cons
     }
 }
 
-template <int S, int G, int U, int R, int RT>
+// Waves 0-3 of the block (the MLP team) wait here until all four have
+// arrived for the k-th time (k = 1, 2, ...): an arrival counter in LDS, read
+// with s_sleep between reads.  The other waves never take part, so the
+// block-wide barrier cannot be used.  The wait is bounded (tens of ms), so
+// that no wave can be kept forever.
+constexpr int kTeamWaves = 4;
+constexpr int kTeamMinTables = 8;
+constexpr int kTeamSpinLimit = 1 << 20;
+__device__ __forceinline__ void team_barrier(unsigned* counter, unsigned k) {
+    typedef __attribute__((address_space(3))) unsigned lds_u32;
+    lds_u32* c = (lds_u32*)counter;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    if ((threadIdx.x & 63) == 0) __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    for (int spin = 0; spin < kTeamSpinLimit; ++spin) {
+        if (__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= kTeamWaves * k) break;
+        __builtin_amdgcn_s_sleep(1);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
+// TEAM: the bags are gathered by waves 4-7 while waves 0-3 run the bottom MLP
+// (they meet at one block-wide barrier before the interaction), so that the
+// gather's chain of dependent loads overlaps the bottom layers; chosen from
+// 8 tables up, where the gather outlasts what 4 MLP waves lose against 8.
+template <int S, int G, int U, int R, int RT, bool TEAM>
 __global__ __launch_bounds__(kFusedThreads) void fused_forward_kernel(FusedArgs fa) {
     using V = Vec<4>;
     constexpr int NT = kFusedThreads;
@@ -287,31 +309,40 @@ __global__ __launch_bounds__(kFusedThreads) void fused_forward_kernel(FusedArgs 
     const int64_t b0 = (int64_t)blockIdx.x * S;
     const int nb = (int)min((int64_t)S, fa.B - b0);
 
+    unsigned* const team_ctr = reinterpret_cast<unsigned*>(wlast + fa.n_small);
+    const int wave = tid >> 6;
+
     // 1. dense rows into buffer 0, zeros in its columns [n0, round_up(n0, 64))
     //    that the first layer's 64-wide k steps read past n0 (every layer
     //    writes the zeros past its own width, mlp_layer), and in the rows of
-    //    samples past the batch; the last layer's weights into LDS
+    //    samples past the batch; the last layer's weights into LDS (threads
+    //    0 .. nt-1)
     const int n0 = fa.bot.dim[0];
     const int w0 = (n0 + 63) & ~63;
-    for (int i = tid; i < S * w0; i += NT) {
-        const int s = i / w0;
-        const int k = i - s * w0;
-        lds_store(buf(0) + s * lda + k, (s < nb && k < n0) ? fa.dense[(b0 + s) * n0 + k] : 0.f);
-    }
-    // one contiguous copy, so that no layer waits on a bias load later
-    for (int i = tid; i < (fa.n_small >> 2); i += NT)
-        lds_store4(wlast + 4 * i, *reinterpret_cast<const floatx4*>(fa.small + 4 * i));
+    auto load_dense_and_tail = [&](int nt) {
+        for (int i = tid; i < S * w0; i += nt) {
+            const int s = i / w0;
+            const int k = i - s * w0;
+            lds_store(buf(0) + s * lda + k, (s < nb && k < n0) ? fa.dense[(b0 + s) * n0 + k] : 0.f);
+        }
+        // one contiguous copy, so that no layer waits on a bias load later
+        for (int i = tid; i < (fa.n_small >> 2); i += nt)
+            lds_store4(wlast + 4 * i, *reinterpret_cast<const floatx4*>(fa.small + 4 * i));
+    };
 
-    // 2. bags of this block's samples into feature rows 1..T
-    {
-        const int lg = tid % G;
-        const int g = tid / G;
+    // 2. bags of this block's samples into feature rows 1..T, by threads
+    //    t0 .. t0 + nt - 1
+    auto gather_all = [&](int t0, int nt) {
+        const int tt = tid - t0;
+        const int lg = tt % G;
+        const int g = tt / G;
+        const int ng = nt / G;
         const int nbag = nb * T;
-        for (int qb = 0; qb < nbag; qb += NG * U) {
+        for (int qb = 0; qb < nbag; qb += ng * U) {
             int q[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int qq = qb + u * NG + g;
+                const int qq = qb + u * ng + g;
                 q[u] = qq < nbag ? qq : -1;
             }
             typename V::T acc[U][1];
@@ -324,18 +355,43 @@ __global__ __launch_bounds__(kFusedThreads) void fused_forward_kernel(FusedArgs 
                 if (lg * 4 < D) V::store(feat + ((size_t)s * F + 1 + t) * LDR + lg * 4, acc[u][0]);
             }
         }
-    }
-    __syncthreads();
+    };
 
     // 3. bottom MLP, ReLU after every layer
     int cur = 0;
     int boff = 0;  // this layer's biases in bias_lds
-    for (int l = 0; l < nbot; ++l) {
-        mlp_layer_any<S>(buf(cur), lda, fa.bot.dim[l], fa.bot.w[l], bias_lds + boff, fa.bot.dim[l + 1], true,
-                         buf(cur ^ 1), lda);
-        boff += (fa.bot.dim[l + 1] + 3) & ~3;
+    if constexpr (TEAM) {
+        if (tid == 0) lds_store(reinterpret_cast<float*>(team_ctr), 0.f);  // the counter's bits: 0
         __syncthreads();
-        cur ^= 1;
+        if (wave < kTeamWaves) {
+            load_dense_and_tail(64 * kTeamWaves);
+            team_barrier(team_ctr, 1);
+            for (int l = 0; l < nbot; ++l) {
+                mlp_layer_any<S, kTeamWaves>(buf(cur), lda, fa.bot.dim[l], fa.bot.w[l], bias_lds + boff,
+                                             fa.bot.dim[l + 1], true, buf(cur ^ 1), lda);
+                boff += (fa.bot.dim[l + 1] + 3) & ~3;
+                cur ^= 1;
+                if (l + 1 < nbot) team_barrier(team_ctr, (unsigned)l + 2);
+            }
+        } else {
+            gather_all(64 * kTeamWaves, NT - 64 * kTeamWaves);
+            for (int l = 0; l < nbot; ++l) {
+                boff += (fa.bot.dim[l + 1] + 3) & ~3;
+                cur ^= 1;
+            }
+        }
+        __syncthreads();
+    } else {
+        load_dense_and_tail(NT);
+        gather_all(0, NT);
+        __syncthreads();
+        for (int l = 0; l < nbot; ++l) {
+            mlp_layer_any<S>(buf(cur), lda, fa.bot.dim[l], fa.bot.w[l], bias_lds + boff, fa.bot.dim[l + 1], true,
+                             buf(cur ^ 1), lda);
+            boff += (fa.bot.dim[l + 1] + 3) & ~3;
+            __syncthreads();
+            cur ^= 1;
+        }
     }
 
     // 4. x into feature row 0 and into R = [x | Z] (the other buffer)
@@ -406,7 +462,8 @@ int fused_lda(const FusedArgs& fa) {
 
 size_t fused_lds_bytes(const FusedArgs& fa, int S) {
     const int F = fa.T + 1;
-    return sizeof(float) * ((size_t)2 * S * fused_lda(fa) + (size_t)S * F * (fa.D + kRowPad) + fa.n_small);
+    // + 4 floats: the MLP team's arrival counter
+    return sizeof(float) * ((size_t)2 * S * fused_lda(fa) + (size_t)S * F * (fa.D + kRowPad) + fa.n_small + 4);
 }
 
 // dst[i] for i < total: the segment of sb holding i, zero in the padding.
@@ -425,14 +482,14 @@ hipError_t launch_pack_small(const SmallBlock& sb, float* dst, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <int S, int G, int U, int R, int RT>
+template <int S, int G, int U, int R, int RT, bool TEAM>
 static hipError_t launch_fused_t(const FusedArgs& fa, hipStream_t s) {
     const size_t lds = fused_lds_bytes(fa, S);
-    hipError_t e = allow_full_lds(fused_forward_kernel<S, G, U, R, RT>);
+    hipError_t e = allow_full_lds(fused_forward_kernel<S, G, U, R, RT, TEAM>);
     if (e != hipSuccess) return e;
     const int64_t blocks = (fa.B + S - 1) / S;
-    hipLaunchKernelGGL((fused_forward_kernel<S, G, U, R, RT>), dim3((unsigned)blocks), dim3(kFusedThreads), lds, s,
-                       fa);
+    hipLaunchKernelGGL((fused_forward_kernel<S, G, U, R, RT, TEAM>), dim3((unsigned)blocks), dim3(kFusedThreads), lds,
+                       s, fa);
     return hipGetLastError();
 }
 
@@ -477,18 +534,36 @@ static hipError_t launch_fused_s(FusedArgs& fa, bool multi_hot, hipStream_t s) {
     // MFMA tile per sample for kMfmaDotsMinTables..32 tables (D a multiple
     // of 16; measured faster there, slower with fewer tables or more tiles)
     const bool mfma_dots = fa.T >= kMfmaDotsMinTables && fa.T <= 32 && fa.D % 16 == 0;
+    // one-index bags: 8 bag slots per lane group, or 1 when the block's bags
+    // fit one slot per group (every slot's bounds are read, used or not);
+    // from kTeamMinTables tables up the bags are gathered beside the bottom
+    // MLP (TEAM; F > 12 always has that many)
+    const bool team = fa.T >= kTeamMinTables;
 #define FUSED_G(G_)                                                                                 \
     case G_:                                                                                        \
         if (F <= 12) {                                                                              \
-            if (multi_hot) return launch_fused_t<S, G_, 4, 4, 0>(fa, s);                            \
-            return launch_fused_t<S, G_, 8, 1, 0>(fa, s);                                           \
+            if (team) {                                                                             \
+                if (multi_hot) return launch_fused_t<S, G_, 4, 4, 0, true>(fa, s);                  \
+                return launch_fused_t<S, G_, 8, 1, 0, true>(fa, s);                                 \
+            }                                                                                       \
+            if (multi_hot) return launch_fused_t<S, G_, 4, 4, 0, false>(fa, s);                     \
+            if (S * fa.T <= kFusedThreads / G_) return launch_fused_t<S, G_, 1, 1, 0, false>(fa, s); \
+            return launch_fused_t<S, G_, 8, 1, 0, false>(fa, s);                                    \
         }                                                                                           \
         if (mfma_dots) {                                                                            \
-            if (multi_hot) return launch_fused_t<S, G_, 4, 4, 32>(fa, s);                           \
-            return launch_fused_t<S, G_, 8, 1, 32>(fa, s);                                          \
+            if (team) {                                                                             \
+                if (multi_hot) return launch_fused_t<S, G_, 4, 4, 32, true>(fa, s);                 \
+                return launch_fused_t<S, G_, 8, 1, 32, true>(fa, s);                                \
+            }                                                                                       \
+            if (multi_hot) return launch_fused_t<S, G_, 4, 4, 32, false>(fa, s);                    \
+            return launch_fused_t<S, G_, 8, 1, 32, false>(fa, s);                                   \
         }                                                                                           \
-        if (multi_hot) return launch_fused_t<S, G_, 4, 4, 4>(fa, s);                                \
-        return launch_fused_t<S, G_, 8, 1, 4>(fa, s);
+        if (team) {                                                                                 \
+            if (multi_hot) return launch_fused_t<S, G_, 4, 4, 4, true>(fa, s);                      \
+            return launch_fused_t<S, G_, 8, 1, 4, true>(fa, s);                                     \
+        }                                                                                           \
+        if (multi_hot) return launch_fused_t<S, G_, 4, 4, 4, false>(fa, s);                         \
+        return launch_fused_t<S, G_, 8, 1, 4, false>(fa, s);
     switch (g) {
         FUSED_G(4)
         FUSED_G(8)
