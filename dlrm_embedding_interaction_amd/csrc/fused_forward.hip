@@ -261,6 +261,77 @@ __device__ __forceinline__ void last_layer(const float* in, int ldi, int K, cons
     }
 }
 
+// The first bottom layer when its input is at most 16 wide (the dense
+// features; one 16-wide chunk per tile of the packed layout) runs on the
+// vector ALUs instead: thread j of the nt threads from t0 computes outputs
+// n = j, j + nt, ... for every sample, as a 16-term dot of the sample's
+// (zero-padded) input row with the output's packed weights, then bias and
+// ReLU.  Its weights are requested at kernel start (first_layer_weights), so
+// that they arrive during the bag gather; with 13 inputs the layer is a few
+// hundred instructions per thread, where a matrix-core pass would pay a ring
+// fill, an epilogue over 32 tiles and a barrier.
+//
+// Output n = 16 t + 4 fg + e sits in lanes 16 fg + 4 kg + e of tile t, which
+// hold its inputs 4 kg .. 4 kg + 3 (zero past the input width).
+template <int NPRE>
+__device__ __forceinline__ void first_layer_weights(const float* __restrict__ Wp, int N, int j, int nt,
+                                                    floatx4 (&w)[NPRE][4]) {
+#pragma unroll
+    for (int i = 0; i < NPRE; ++i) {
+        const int n0 = j + i * nt;
+        const int n = n0 < N ? n0 : 0;
+        const int t = n >> 4, r = n & 15;
+#pragma unroll
+        for (int kg = 0; kg < 4; ++kg)
+            w[i][kg] = ld_global<floatx4>(Wp + ((size_t)t * 64 + 16 * (r >> 2) + 4 * kg + (r & 3)) * 4);
+    }
+}
+
+template <int S, int NPRE>
+__device__ __forceinline__ void first_layer_valu(const float* in, int ldi, const float* __restrict__ Wp,
+                                                 const float* bias, int N, float* out, int ldo, int t0, int nt,
+                                                 const floatx4 (&wpre)[NPRE][4]) {
+    const int j = threadIdx.x - t0;
+    const int npad = (N + 63) & ~63;
+    for (int i = 0; j + i * nt < npad; ++i) {
+        const int n = j + i * nt;
+        if (n >= N) {
+            // columns [N, round_up(N, 64)) the next layer's k steps read
+#pragma unroll
+            for (int s = 0; s < S; ++s) lds_store(out + s * ldo + n, 0.f);
+            continue;
+        }
+        floatx4 w[4];
+        if (i < NPRE) {
+#pragma unroll
+            for (int kg = 0; kg < 4; ++kg) w[kg] = wpre[i < NPRE ? i : 0][kg];
+        } else {
+            floatx4 wl[1][4];
+            first_layer_weights<1>(Wp, N, n, 0, wl);
+#pragma unroll
+            for (int kg = 0; kg < 4; ++kg) w[kg] = wl[0][kg];
+        }
+        const float bv = lds_load(bias + n);
+        // sample s + 1's input row is requested before sample s's dots
+        floatx4 a[2][4];
+#pragma unroll
+        for (int kg = 0; kg < 4; ++kg) a[0][kg] = lds_load4(in + 4 * kg);
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+            if (s + 1 < S) {
+#pragma unroll
+                for (int kg = 0; kg < 4; ++kg) a[(s + 1) & 1][kg] = lds_load4(in + (s + 1) * ldi + 4 * kg);
+            }
+            float acc = 0.f;
+#pragma unroll
+            for (int kg = 0; kg < 4; ++kg)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) acc = fmaf(a[s & 1][kg][q], w[kg][q], acc);
+            lds_store(out + s * ldo + n, fmaxf(acc + bv, 0.f));
+        }
+    }
+}
+
 // Waves 0-3 of the block (the MLP team) wait here until all four have
 // arrived for the k-th time (k = 1, 2, ...): an arrival counter in LDS, read
 // with s_sleep between reads.  The other waves never take part, so the
@@ -311,6 +382,7 @@ __global__ __launch_bounds__(kFusedThreads) void fused_forward_kernel(FusedArgs 
 
     unsigned* const team_ctr = reinterpret_cast<unsigned*>(wlast + fa.n_small);
     const int wave = tid >> 6;
+    const bool valu0 = fa.bot.dim[0] <= 16;  // the first layer on the vector ALUs
 
     // 1. dense rows into buffer 0, zeros in its columns [n0, round_up(n0, 64))
     //    that the first layer's 64-wide k steps read past n0 (every layer
@@ -364,11 +436,17 @@ __global__ __launch_bounds__(kFusedThreads) void fused_forward_kernel(FusedArgs 
         if (tid == 0) lds_store(reinterpret_cast<float*>(team_ctr), 0.f);  // the counter's bits: 0
         __syncthreads();
         if (wave < kTeamWaves) {
+            floatx4 w0[2][4];
+            if (valu0) first_layer_weights<2>(fa.bot.w[0], fa.bot.dim[1], tid, 64 * kTeamWaves, w0);
             load_dense_and_tail(64 * kTeamWaves);
             team_barrier(team_ctr, 1);
             for (int l = 0; l < nbot; ++l) {
-                mlp_layer_any<S, kTeamWaves>(buf(cur), lda, fa.bot.dim[l], fa.bot.w[l], bias_lds + boff,
-                                             fa.bot.dim[l + 1], true, buf(cur ^ 1), lda);
+                if (l == 0 && valu0)
+                    first_layer_valu<S, 2>(buf(cur), lda, fa.bot.w[0], bias_lds, fa.bot.dim[1], buf(cur ^ 1), lda, 0,
+                                           64 * kTeamWaves, w0);
+                else
+                    mlp_layer_any<S, kTeamWaves>(buf(cur), lda, fa.bot.dim[l], fa.bot.w[l], bias_lds + boff,
+                                                 fa.bot.dim[l + 1], true, buf(cur ^ 1), lda);
                 boff += (fa.bot.dim[l + 1] + 3) & ~3;
                 cur ^= 1;
                 if (l + 1 < nbot) team_barrier(team_ctr, (unsigned)l + 2);
@@ -382,12 +460,18 @@ __global__ __launch_bounds__(kFusedThreads) void fused_forward_kernel(FusedArgs 
         }
         __syncthreads();
     } else {
+        floatx4 w0[1][4];
+        if (valu0) first_layer_weights<1>(fa.bot.w[0], fa.bot.dim[1], tid, NT, w0);
         load_dense_and_tail(NT);
         gather_all(0, NT);
         __syncthreads();
         for (int l = 0; l < nbot; ++l) {
-            mlp_layer_any<S>(buf(cur), lda, fa.bot.dim[l], fa.bot.w[l], bias_lds + boff, fa.bot.dim[l + 1], true,
-                             buf(cur ^ 1), lda);
+            if (l == 0 && valu0)
+                first_layer_valu<S, 1>(buf(cur), lda, fa.bot.w[0], bias_lds, fa.bot.dim[1], buf(cur ^ 1), lda, 0, NT,
+                                       w0);
+            else
+                mlp_layer_any<S>(buf(cur), lda, fa.bot.dim[l], fa.bot.w[l], bias_lds + boff, fa.bot.dim[l + 1], true,
+                                 buf(cur ^ 1), lda);
             boff += (fa.bot.dim[l + 1] + 3) & ~3;
             __syncthreads();
             cur ^= 1;
