@@ -622,6 +622,7 @@ static hipError_t launch_fused_s(FusedArgs& fa, bool multi_hot, hipStream_t s) {
     // fit one slot per group (every slot's bounds are read, used or not);
     // from kTeamMinTables tables up the bags are gathered beside the bottom
     // MLP (TEAM; F > 12 always has that many)
+    static_assert(kTeamMinTables <= 12, "more than 11 tables always take the TEAM kernels");
     const bool team = fa.T >= kTeamMinTables;
 #define FUSED_G(G_)                                                                                 \
     case G_:                                                                                        \
@@ -635,19 +636,11 @@ static hipError_t launch_fused_s(FusedArgs& fa, bool multi_hot, hipStream_t s) {
             return launch_fused_t<S, G_, 8, 1, 0, false>(fa, s);                                    \
         }                                                                                           \
         if (mfma_dots) {                                                                            \
-            if (team) {                                                                             \
-                if (multi_hot) return launch_fused_t<S, G_, 4, 4, 32, true>(fa, s);                 \
-                return launch_fused_t<S, G_, 8, 1, 32, true>(fa, s);                                \
-            }                                                                                       \
-            if (multi_hot) return launch_fused_t<S, G_, 4, 4, 32, false>(fa, s);                    \
-            return launch_fused_t<S, G_, 8, 1, 32, false>(fa, s);                                   \
+            if (multi_hot) return launch_fused_t<S, G_, 4, 4, 32, true>(fa, s);                     \
+            return launch_fused_t<S, G_, 8, 1, 32, true>(fa, s);                                    \
         }                                                                                           \
-        if (team) {                                                                                 \
-            if (multi_hot) return launch_fused_t<S, G_, 4, 4, 4, true>(fa, s);                      \
-            return launch_fused_t<S, G_, 8, 1, 4, true>(fa, s);                                     \
-        }                                                                                           \
-        if (multi_hot) return launch_fused_t<S, G_, 4, 4, 4, false>(fa, s);                         \
-        return launch_fused_t<S, G_, 8, 1, 4, false>(fa, s);
+        if (multi_hot) return launch_fused_t<S, G_, 4, 4, 4, true>(fa, s);                          \
+        return launch_fused_t<S, G_, 8, 1, 4, true>(fa, s);
     switch (g) {
         FUSED_G(4)
         FUSED_G(8)

@@ -408,6 +408,24 @@ def test_forward_odd_layer_shapes_sixteen_samples_per_block(ln_bot, hidden_top, 
     inp = di.make_inputs(w)
     _forward_check(inp, on_gpu(inp), orc, path="fused")
 
+@pytest.mark.parametrize("T", [9, 20])
+@pytest.mark.parametrize("bag", [1, 2])
+@pytest.mark.parametrize("B", [77, 2100])
+@pytest.mark.parametrize("ln_bot,hidden_top,D", [((13, 37, 16), (), 16), ((3, 300, 100, 48), (129, 17), 48),
+                                                 ((40, 24, 20, 28, 32, 36, 40, 44, 52), (8,) * 7, 52)])
+def test_forward_bags_gathered_beside_the_bottom_mlp(ln_bot, hidden_top, D, B, bag, T, orc):
+    """From 8 tables the single launch gathers the bags on half its waves while
+    the other half runs the bottom MLP: odd widths, a first layer on the vector
+    ALUs (13 or 3 inputs) or on the matrix cores (40 inputs), eight bottom
+    layers, one- and two-index bags, 8 and 16 samples per block, a ragged last
+    block."""
+    w = di.custom(f"team_{T}_{len(ln_bot)}_{D}_{bag}", B, ln_bot[0], T, 700, D, bag, ln_bot, hidden_top=hidden_top,
+                  cfg_id=28)
+    inp = di.make_inputs(w)
+    log(f"team T={T} B={B} bag={bag} ln_bot={ln_bot}")
+    _forward_check(inp, on_gpu(inp), orc, path="fused")
+
+
 
 @pytest.mark.parametrize("path", ["fused", "layered"])
 def test_forward_zero_last_layer_gives_exactly_half(path):
