@@ -255,6 +255,8 @@ hipError_t launch_interact(const TableArgs* ta, const float* emb, int T, int D, 
         return launch_gram_interact(*ta, T, D, B, aligned16, x, ld_x, out, ld_out, col_x, col_z, s);
     const RowShape rs = row_shape(D, aligned16);
     const int spb = interact_samples_per_block(T, D, B);
+    // one-index bags: 4 bag slots per lane group, or 1 when a block's bags fit
+    // one per group (every slot's bounds are read, used or not);
     // multi-hot bags: one bag per lane group at a time, 8 row indices and rows
     // per step (measured on MI355X at 26 tables, bag 20, Zipf, batch 65536:
     // 1795 us against 1852 us with 4 bags x 4 rows, which holds more
@@ -280,6 +282,9 @@ hipError_t launch_interact(const TableArgs* ta, const float* emb, int T, int D, 
                                                                     col_x, col_z, dsplit, s);                  \
     if (multi_hot) return launch_interact_t<V, G, C, 1, 8, true, RT>(t, emb, T, D, B, spb, x, ld_x, out, ld_out, \
                                                                      col_x, col_z, dsplit, s);                 \
+    if (spb * T <= kBlock / G)                                                                                 \
+        return launch_interact_t<V, G, C, 1, 1, true, RT>(t, emb, T, D, B, spb, x, ld_x, out, ld_out, col_x,    \
+                                                          col_z, dsplit, s);                                   \
     return launch_interact_t<V, G, C, 4, 1, true, RT>(t, emb, T, D, B, spb, x, ld_x, out, ld_out, col_x, col_z, \
                                                       dsplit, s);
 #define CALL_I(V, G, C)          \
