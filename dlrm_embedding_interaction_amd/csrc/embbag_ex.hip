@@ -42,27 +42,42 @@ __global__ __launch_bounds__(kBlock) void embbag_ex_kernel(BagArgs ba, int T, in
     typename V::T acc[U][C];
     const typename V::T init = (mode == DLRM_BAG_MAX) ? V::splat(-INFINITY) : V::zero();
     int maxlen = 0;
+    // Bag bounds in passes over the U slots, every load of a pass in flight
+    // together: the tables' arguments, then both offsets of each bag (no load
+    // under a per-slot branch, where waiting for it would also wait for every
+    // older load).  A slot past the last bag reads bag 0 and gets length 0.
+    const IDX* op[U];
+    int64_t bb[U], nid[U];
+    const float* psw[U];
+    const void* ix[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         q[u] = base + u * NG + g;
-        len[u] = 0;
+        const int64_t qq = q[u] < nbags ? q[u] : 0;
+        bb[u] = qq / T;
+        const int t = (int)(qq - bb[u] * T);
+        op[u] = reinterpret_cast<const IDX*>(ba.off[t]);
+        wp[u] = ba.w[t];
+        ix[u] = ba.idx[t];
+        psw[u] = ba.psw[t];
+        pad[u] = ba.pad[t];
+        nid[u] = ba.nidx[t];
+    }
+    IDX s0[U], e0[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t be = (last_off || bb[u] + 1 < B) ? bb[u] + 1 : bb[u];
+        s0[u] = ld_global<IDX>(op[u] + bb[u]);
+        e0[u] = ld_global<IDX>(op[u] + be);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t s = s0[u];
+        const int64_t e = (last_off || bb[u] + 1 < B) ? (int64_t)e0[u] : nid[u];
+        len[u] = q[u] < nbags ? (int)(e - s) : 0;
         cnt[u] = 0;
-        wp[u] = nullptr;
-        ip[u] = nullptr;
-        ps[u] = nullptr;
-        pad[u] = -1;
-        if (q[u] < nbags) {
-            const int64_t b = q[u] / T;
-            const int t = (int)(q[u] - b * T);
-            const IDX* off = reinterpret_cast<const IDX*>(ba.off[t]);
-            const int64_t s = ld_idx<IDX>(off, b);
-            const int64_t e = last_off ? ld_idx<IDX>(off, b + 1) : ((b + 1 < B) ? ld_idx<IDX>(off, b + 1) : ba.nidx[t]);
-            len[u] = (int)(e - s);
-            wp[u] = ba.w[t];
-            ip[u] = reinterpret_cast<const IDX*>(ba.idx[t]) + s;
-            ps[u] = ba.psw[t] ? ba.psw[t] + s : nullptr;
-            pad[u] = ba.pad[t];
-        }
+        ip[u] = reinterpret_cast<const IDX*>(ix[u]) + s;
+        ps[u] = psw[u] ? psw[u] + s : nullptr;
         maxlen = max(maxlen, len[u]);
 #pragma unroll
         for (int c = 0; c < C; ++c) acc[u][c] = init;
