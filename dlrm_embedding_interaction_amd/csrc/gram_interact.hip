@@ -26,6 +26,12 @@
 //    l holds feature 16 blk + (l % 16) for k slot l / 16;  16-byte chunk c of
 //    row f is kept at chunk c ^ (f % (D/4)), so that neither the writes (one
 //    row per 16 lanes) nor the reads (16 rows per 16 lanes) meet in a bank;
+//  * LITE (rows of at most 64 floats): the rows go straight from memory into
+//    the wave's LDS by 16-byte DMA copies (global_load_lds), one sample at a
+//    time, with no register ring, and Z is staged where the rows were.  That
+//    frees the ring's registers and LDS for 4 waves per SIMD instead of 2:
+//    random row reads scale with the waves issuing them more than with the
+//    bytes each has in flight (batch 16384 x 32 tables: 41.4 -> 35.8 us);
 //  * because G is symmetric, the same registers are both MFMA operands: tile
 //    (I, J) multiplies feature block I by block J, and the tile above the
 //    diagonal is never formed (NB = 2: tiles (0,0), (1,0), (1,1));
@@ -59,13 +65,16 @@ struct GramTable {
 
 // Bytes of one wave's LDS region: the row addresses of its NS samples, one
 // sample's FP staged rows, then one sample's Z (at most FP(FP-1)/2 floats).
-template <int D, int FP, int NS>
+template <int D, int FP, int NS, bool LITE>
 constexpr int gram_wave_lds() {
-    return (NS * FP * 8 + 15) / 16 * 16 + FP * D * 4 + (FP * (FP - 1) / 2 + 3) / 4 * 16;
+    return (NS * FP * 8 + 15) / 16 * 16 + FP * D * 4 + (LITE ? 0 : (FP * (FP - 1) / 2 + 3) / 4 * 16);
 }
 
-template <int D, int NB, bool EXTRA, int NS, int PD>
-__global__ __launch_bounds__(kGramThreads) void gram_interact_kernel(TableArgs ta, int T, int64_t B,
+// 1 KiB of zeros: where an empty bag's row is copied from
+__device__ __attribute__((aligned(16))) float g_gram_zero_row[256];
+
+template <int D, int NB, bool EXTRA, int NS, int PD, bool LITE>
+__global__ __launch_bounds__(kGramThreads) __attribute__((amdgpu_waves_per_eu(LITE ? 4 : 1, 8))) void gram_interact_kernel(TableArgs ta, int T, int64_t B,
                                                                      const float* __restrict__ x, int64_t ld_x,
                                                                      float* __restrict__ out, int64_t ld_out,
                                                                      int col_x, int col_z) {
@@ -91,10 +100,10 @@ __global__ __launch_bounds__(kGramThreads) void gram_interact_kernel(TableArgs t
     if (b0 >= B) return;  // the whole wave; no barrier follows
     const int ns = (int)min((int64_t)NS, B - b0);
     char* const region = reinterpret_cast<char*>(lds4) + kGramMaxTables * sizeof(GramTable) +
-                         wave * gram_wave_lds<D, FP, NS>();
+                         wave * gram_wave_lds<D, FP, NS, LITE>();
     int64_t* const rowptr = reinterpret_cast<int64_t*>(region);                     // [NS][FP]
     float* const buf = reinterpret_cast<float*>(region + (NS * FP * 8 + 15) / 16 * 16);  // [FP][D]
-    float* const zbuf = buf + FP * D;                                                   // [P]
+    float* const zbuf = LITE ? buf : buf + FP * D;  // [P]; with LITE after every read of the rows
     const int P = F * (F - 1) / 2;
     // Z rows are written 16 bytes per lane when every row starts 16-byte aligned
     const bool vec_z = ((reinterpret_cast<uintptr_t>(out + col_z) | (uintptr_t)(ld_out * 4)) & 15) == 0;
@@ -267,16 +276,52 @@ __global__ __launch_bounds__(kGramThreads) void gram_interact_kernel(TableArgs t
                 v[k] = take ? w : floatx4{0.f, 0.f, 0.f, 0.f};
             }
         };
-        floatx4 ring[PD][NLD];
+        if constexpr (LITE) {
+            // rows copied into the wave's LDS by DMA (no register ring): lane
+            // l of a copy writes bytes [16 l, 16 l + 16) after the copy's
+            // base, i.e. row RPI k + l / CPR, chunk l % CPR, read from the
+            // swizzled chunk of the table row; lanes past the FP staged rows
+            // copy nothing.  The row addresses are read from LDS before the
+            // first copy (a later LDS read would wait for the copies).
+#pragma unroll 1
+            for (int s = 0; s < ns; ++s) {
+                int64_t pr[NLD];
 #pragma unroll
-        for (int s = 0; s < PD && s < NS; ++s) issue(s, ring[s]);
+                for (int k = 0; k < NLD; ++k) {
+                    const int f = RPI * k + lrow;
+                    pr[k] = lds_load8(rowptr + s * FP + min(f, FP - 1));
+                }
 #pragma unroll
-        for (int s = 0; s < NS; ++s) {
-            if (s >= ns) break;
-            stage(ring[s % PD]);
-            if (s + PD < NS) issue(s + PD, ring[s % PD]);
-            compute(s);
-            done_reading();
+                for (int k = 0; k < NLD; ++k) {
+                    const int f = RPI * k + lrow;
+                    if (f < FP) {
+                        const char* src = pr[k] != 0
+                                              ? reinterpret_cast<const char*>(pr[k]) + 16 * (lchunk ^ swz(f))
+                                              : reinterpret_cast<const char*>(g_gram_zero_row) + 16 * lchunk;
+                        __builtin_amdgcn_global_load_lds(
+                            (const __attribute__((address_space(1))) void*)src,
+                            (__attribute__((address_space(3))) void*)(lds_float*)(buf + k * RPI * D), 16, 0, 0);
+                    }
+                }
+                __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the copies have landed
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                compute(s);
+                done_reading();
+            }
+        } else {
+            floatx4 ring[PD][NLD];
+#pragma unroll
+            for (int s = 0; s < PD && s < NS; ++s) issue(s, ring[s]);
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                if (s >= ns) break;
+                stage(ring[s % PD]);
+                if (s + PD < NS) issue(s + PD, ring[s % PD]);
+                compute(s);
+                done_reading();
+            }
         }
     } else {
         // bags of any length: each bag summed in a loop, one sample at a time
@@ -309,22 +354,22 @@ __global__ __launch_bounds__(kGramThreads) void gram_interact_kernel(TableArgs t
     }
 }
 
-template <int D, int NB, bool EXTRA, int NS>
+template <int D, int NB, bool EXTRA, int NS, bool LITE>
 hipError_t launch_gram_t(const TableArgs& ta, int T, int64_t B, const float* x, int64_t ld_x, float* out,
                          int64_t ld_out, int col_x, int col_z, hipStream_t s) {
     constexpr int FP = 16 * NB + (EXTRA ? 1 : 0);
     constexpr int NLD = (FP + 64 / (D / 4) - 1) / (64 / (D / 4));
     // samples in flight per wave: as many as about 40 ring registers allow
     constexpr int PD = NLD <= 4 ? 3 : 2;
-    constexpr size_t lds = kGramMaxTables * sizeof(GramTable) + kGramWaves * gram_wave_lds<D, FP, NS>();
+    constexpr size_t lds = kGramMaxTables * sizeof(GramTable) + kGramWaves * gram_wave_lds<D, FP, NS, LITE>();
     const int64_t waves = (B + NS - 1) / NS;
     const int64_t blocks = (waves + kGramWaves - 1) / kGramWaves;
     static_assert(lds <= kFusedMaxLds, "LDS of one block");
     if (lds > 64 * 1024) {
-        hipError_t e = allow_full_lds(gram_interact_kernel<D, NB, EXTRA, NS, PD>);
+        hipError_t e = allow_full_lds(gram_interact_kernel<D, NB, EXTRA, NS, PD, LITE>);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((gram_interact_kernel<D, NB, EXTRA, NS, PD>), dim3((unsigned)blocks), dim3(kGramThreads), lds,
+    hipLaunchKernelGGL((gram_interact_kernel<D, NB, EXTRA, NS, PD, LITE>), dim3((unsigned)blocks), dim3(kGramThreads), lds,
                        s, ta, T, B, x, ld_x, out, ld_out, col_x, col_z);
     return hipGetLastError();
 }
@@ -334,15 +379,16 @@ hipError_t launch_gram_ns(const TableArgs& ta, int T, int64_t B, const float* x,
                           int64_t ld_out, int col_x, int col_z, hipStream_t s) {
     // samples per wave: so many that every wave is resident at once and pays
     // the bag-bound and index round trips only once (256 CUs x 4 SIMDs x the
-    // waves per SIMD the registers allow: about 4 with one 16-feature block,
-    // 2 with more; measured at batch 16384: 8 tables 13.6 -> 12.7 us with 4,
-    // 16 tables 18.4 -> 19.8 us); at most 8 samples per wave
-    constexpr int64_t kResidentWaves = 1024 * (NB == 1 && !EXTRA ? 4 : 2);
+    // waves per SIMD the registers and LDS allow: 4 with the DMA-staged rows
+    // (LITE, rows of at most 64 floats) or with one 16-feature block, 2
+    // otherwise); at most 8 samples per wave
+    constexpr bool LITE = D <= 64;
+    constexpr int64_t kResidentWaves = 1024 * (LITE || (NB == 1 && !EXTRA) ? 4 : 2);
     const int64_t want = (B + kResidentWaves - 1) / kResidentWaves;
-    if (want <= 1) return launch_gram_t<D, NB, EXTRA, 1>(ta, T, B, x, ld_x, out, ld_out, col_x, col_z, s);
-    if (want <= 2) return launch_gram_t<D, NB, EXTRA, 2>(ta, T, B, x, ld_x, out, ld_out, col_x, col_z, s);
-    if (want <= 4) return launch_gram_t<D, NB, EXTRA, 4>(ta, T, B, x, ld_x, out, ld_out, col_x, col_z, s);
-    return launch_gram_t<D, NB, EXTRA, 8>(ta, T, B, x, ld_x, out, ld_out, col_x, col_z, s);
+    if (want <= 1) return launch_gram_t<D, NB, EXTRA, 1, LITE>(ta, T, B, x, ld_x, out, ld_out, col_x, col_z, s);
+    if (want <= 2) return launch_gram_t<D, NB, EXTRA, 2, LITE>(ta, T, B, x, ld_x, out, ld_out, col_x, col_z, s);
+    if (want <= 4) return launch_gram_t<D, NB, EXTRA, 4, LITE>(ta, T, B, x, ld_x, out, ld_out, col_x, col_z, s);
+    return launch_gram_t<D, NB, EXTRA, 8, LITE>(ta, T, B, x, ld_x, out, ld_out, col_x, col_z, s);
 }
 
 template <int D>
