@@ -14,11 +14,17 @@
 //  * every Linear layer streams its weight rows straight from L2 into
 //    registers (each weight is read once per block and used for all S
 //    samples) and multiplies them on the matrix cores with
-//    v_mfma_f32_4x4x1f32: one instruction is 16 blocks of 4x4x1, and lane
-//    l = 16 fg + 4 kg + e supplies W[f = 4 fg + e][k = 4 kg + q] as A and
-//    act[sample e][k] as B, so one instruction covers 16 features x 4 samples
-//    x 4 k values at the full fp32 MFMA rate even with 4-sample groups; the
-//    4 k groups are added afterwards with two DPP row rotations;
+//    v_mfma_f32_4x4x1f32, one instruction being 16 blocks of 4x4x1:
+//    - layers of more than 128 outputs: the instruction's A-broadcast field
+//      (CBSZ = 1) lets both blocks of each pair take the weights of one of
+//      them (ABID 0 or 1), so lane l = 8 m + 4 h + i holds W[4 m + i][k] for
+//      two values of k (h = 0, 1), every lane holds act[sample l % 8][k] as
+//      B, and one instruction covers 32 features x 8 samples x 1 k with the
+//      outputs complete in the lanes (4 consecutive features of one sample);
+//    - narrower layers: lane l = 16 fg + 4 kg + e supplies
+//      W[f = 4 fg + e][k = 4 kg + q] as A and act[sample e][k] as B, one
+//      instruction covering 16 features x 4 samples x 4 k values; the 4 k
+//      groups are added afterwards with two DPP row rotations;
 //  * the bags are gathered with the same lane-group code as the standalone
 //    bag kernel and the dots reuse the interaction kernel's LDS routine;
 //  * nothing leaves the block but the S sigmoid outputs.
@@ -64,22 +70,31 @@ __device__ __forceinline__ void zero_columns(float* out, int ldo, int c0, int c1
     }
 }
 
-// Packed weights of one layer (N, K): tiles of 16 output features x 16 inputs,
-// tile (t, kc) at float offset (t * ceil(K / 16) + kc) * 256, holding for lane
-// l = 16 fg + 4 kg + e the four weights W[16 t + 4 fg + e][16 kc + 4 kg + q],
-// q = 0..3, and zeros past N or K.
+// Packed weights of one layer (N, K), zeros past N or K; each chunk is 64
+// lanes x 4 floats (1 KiB, one wave load):
+//  * narrow layers (N <= 128): tiles of 16 output features x 16 inputs, chunk
+//    (t, kc) at float offset (t * ceil(K / 16) + kc) * 256, holding for lane
+//    l = 16 fg + 4 kg + e the weights W[16 t + 4 fg + e][16 kc + 4 kg + q];
+//  * wide layers (N > 128): tiles of 32 output features x 8 inputs, chunk
+//    (t, kc) at float offset (t * ceil(K / 8) + kc) * 256, holding for lane
+//    l = 8 m + 4 h + i the weights W[32 t + 4 m + i][8 kc + 4 h + q];
+// q = 0..3.  A narrow layer of 64 outputs keeps 4 tiles for 8 waves, where 32-wide tiles
+// would leave 6 of them idle.
+__host__ __device__ inline bool wide_tiles(int N) { return N > 128; }
+
 __global__ __launch_bounds__(kBlock) void pack_layer_kernel(const float* __restrict__ W, int N, int K,
                                                             float* __restrict__ packed) {
-    const int nkc = (K + 15) >> 4;
-    const int64_t total = (int64_t)((N + 15) >> 4) * nkc * 64;
+    const bool wide = wide_tiles(N);
+    const int nkc = wide ? (K + 7) >> 3 : (K + 15) >> 4;
+    const int64_t total = (int64_t)(wide ? (N + 31) >> 5 : (N + 15) >> 4) * nkc * 64;
     const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
     if (i >= total) return;
     const int lane = (int)(i & 63);
     const int64_t tk = i >> 6;
     const int t = (int)(tk / nkc);
     const int kc = (int)(tk - (int64_t)t * nkc);
-    const int n = 16 * t + 4 * (lane >> 4) + (lane & 3);
-    const int k0 = 16 * kc + 4 * ((lane >> 2) & 3);
+    const int n = wide ? 32 * t + 4 * (lane >> 3) + (lane & 3) : 16 * t + 4 * (lane >> 4) + (lane & 3);
+    const int k0 = wide ? 8 * kc + 4 * ((lane >> 2) & 1) : 16 * kc + 4 * ((lane >> 2) & 3);
     floatx4 v;
 #pragma unroll
     for (int q = 0; q < 4; ++q) v[q] = (n < N && k0 + q < K) ? W[(int64_t)n * K + k0 + q] : 0.f;
@@ -87,8 +102,8 @@ __global__ __launch_bounds__(kBlock) void pack_layer_kernel(const float* __restr
 }
 
 // out[s][n] = act(sum_k in[s][k] W[n][k] + bias[n]) for s < S, n < N, with in,
-// out and bias in LDS (row strides ldi, ldo) and W packed as above.  The N outputs
-// form tiles of 16 features; wave w (of the NW waves 0 .. NW-1 that run the
+// out and bias in LDS (row strides ldi, ldo) and W packed as above (a narrow
+// layer, N <= 128).  The N outputs form tiles of 16 features; wave w (of the NW waves 0 .. NW-1 that run the
 // layer) takes tiles w, w + NW, ... in passes of TW tiles.  One step covers KU chunks of 16 k values; the weights of a step are
 // requested PD steps ahead into a register ring whose slots are fixed at
 // compile time (no register copies, so the wait before a step's MFMAs covers
@@ -211,16 +226,137 @@ __device__ __forceinline__ void mlp_layer(const float* in, int ldi, int K, const
     zero_columns<S, 64 * NW>(out, ldo, (N + 15) & ~15, (N + 63) & ~63);
 }
 
-// Layer dispatch: TW = tiles per wave and pass, KU chunks of 16 k per step and
-// PD steps in flight.  Layers of one or two tiles per wave keep 2 steps (8
-// weight loads, 8 KiB per wave) in flight: measured on MI355X, deeper rings
-// there leave the waves stalled on the CU's vector-memory queue, which holds
-// up their MFMAs too (8 samples: 512->256 layer 6.9 -> 6.3 us, 256->64 2.6 ->
-// 2.1 us; 16 samples: batch 4096 x 4 tables 44.3 -> 42.5 us per forward);
-// four-tile layers keep 6 steps.
+// The same for a layer packed in 32-wide tiles (more than 128 outputs).  Each
+// instruction multiplies 32 features by one k for 8 samples: A-broadcast
+// (CBSZ = 1) hands each pair of blocks (one pair per 4 features) the weights
+// held by one of them, ABID 0 taking the lanes of the 4 k values of chunk
+// half h = 0 and ABID 1 those of h = 1, and every lane's B is its own sample
+// l % 8.  A step reads, per chunk and group of 8 samples, two float4 of
+// activations per lane (k 0-3 and 4-7 of the chunk).  The halves h = 0, 1
+// accumulate apart (two independent MFMA chains per tile and group).  Lane
+// l = 8 m + 4 sg + j then holds in accumulator register i the complete sum
+// for feature 32 t + 4 m + i and sample 8 g + 4 sg + j, so the epilogue is
+// bias, activation and one 16-byte LDS store per tile and group, with no
+// cross-lane sums.
+template <int S, int TW, int KU, int PD, int NW>
+__device__ __forceinline__ void mlp_layer_wide(const float* in, int ldi, int K, const float* __restrict__ Wp,
+                                          const float* bias, int N, bool relu, float* out, int ldo) {
+    static_assert(S % 8 == 0, "groups of 8 samples");
+    constexpr int SG = S / 8;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int m = lane >> 3;   // outputs 4 m .. 4 m + 3 of a tile
+    const int s8 = lane & 7;   // sample s8 of each group of 8
+    const int ntile = (N + 31) >> 5;
+    const int nkc = (K + 7) >> 3;
+    const int nkb = (nkc + KU - 1) / KU;
+    const float* arow[SG];
+#pragma unroll
+    for (int g = 0; g < SG; ++g) arow[g] = in + (8 * g + s8) * ldi;
+
+    const __amdgpu_buffer_rsrc_t wr = weight_rsrc(Wp, (uint32_t)ntile * nkc * 1024u);
+    for (int t0 = 0; t0 < ntile; t0 += NW * TW) {
+        if (t0 + wave >= ntile) break;
+        uint32_t wtile[TW];
+        floatx4 acc[TW][SG][2];
+#pragma unroll
+        for (int u = 0; u < TW; ++u) {
+            const int t = t0 + wave + NW * u;
+            wtile[u] = t < ntile ? ((uint32_t)t * nkc * 64u + lane) * 16u : kOutOfRange;
+#pragma unroll
+            for (int g = 0; g < SG; ++g) acc[u][g][0] = acc[u][g][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+        }
+        floatx4 ring[PD][TW][KU];
+        auto loadw = [&](int kb, floatx4 (&w)[TW][KU]) {
+#pragma unroll
+            for (int u = 0; u < TW; ++u)
+#pragma unroll
+                for (int c = 0; c < KU; ++c) {
+                    const int ch = kb * KU + c;
+                    w[u][c] = buffer_load4(wr, ch < nkc ? wtile[u] + (uint32_t)ch * 1024u : kOutOfRange);
+                }
+        };
+        auto step = [&](int kb, const floatx4 (&w)[TW][KU]) {
+            floatx4 a[KU][SG][2];
+#pragma unroll
+            for (int c = 0; c < KU; ++c)
+#pragma unroll
+                for (int g = 0; g < SG; ++g)
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) a[c][g][h] = lds_load4(arow[g] + (kb * KU + c) * 8 + 4 * h);
+#pragma unroll
+            for (int c = 0; c < KU; ++c)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+#pragma unroll
+                    for (int u = 0; u < TW; ++u)
+#pragma unroll
+                        for (int g = 0; g < SG; ++g) {
+                            acc[u][g][0] = __builtin_amdgcn_mfma_f32_4x4x1f32(w[u][c][q], a[c][g][0][q], acc[u][g][0], 1, 0, 0);
+                            acc[u][g][1] = __builtin_amdgcn_mfma_f32_4x4x1f32(w[u][c][q], a[c][g][1][q], acc[u][g][1], 1, 1, 0);
+                        }
+        };
+#pragma unroll
+        for (int p = 0; p < PD; ++p) loadw(p, ring[p]);
+        const int trips = nkb / PD;
+        for (int tr = 0; tr < trips; ++tr) {
+#pragma unroll
+            for (int p = 0; p < PD; ++p) {
+                const int kb = tr * PD + p;
+                step(kb, ring[p]);
+                loadw(kb + PD, ring[p]);
+            }
+        }
+        const int rest = nkb - trips * PD;
+#pragma unroll
+        for (int p = 0; p < PD; ++p)
+            if (p < rest) step(trips * PD + p, ring[p]);
+#pragma unroll
+        for (int u = 0; u < TW; ++u) {
+            const int t = t0 + wave + NW * u;
+            if (t >= ntile) break;
+            const int n = 32 * t + 4 * m;
+            const floatx4 bv = n < N ? lds_load4(bias + n) : floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int g = 0; g < SG; ++g) {
+                const floatx4 v = acc[u][g][0] + acc[u][g][1] + bv;
+                floatx4 y;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) y[i] = n + i < N ? (relu ? fmaxf(v[i], 0.f) : v[i]) : 0.f;
+                lds_store4(out + (8 * g + s8) * ldo + n, y);
+            }
+        }
+    }
+    zero_columns<S, 64 * NW>(out, ldo, (N + 31) & ~31, (N + 63) & ~63);
+}
+
+// Layer dispatch: TW = tiles per wave and pass, KU chunks per step and PD
+// steps in flight.  Narrow layers (16-wide tiles, chunks of 16 k) of one or
+// two tiles per wave keep 2 steps (8 weight loads, 8 KiB per wave) in flight:
+// measured on MI355X, deeper rings there leave the waves stalled on the CU's
+// vector-memory queue, which holds up their MFMAs too (8 samples: 512->256
+// layer 6.9 -> 6.3 us, 256->64 2.6 -> 2.1 us; 16 samples: batch 4096 x 4
+// tables 44.3 -> 42.5 us per forward); four-tile layers keep 6 steps.  Wide
+// layers (32-wide tiles, chunks of 8 k): one tile per wave keeps 2 steps of 4
+// chunks, two tiles 6 steps of one chunk each (12 KiB; 8 and 24 KiB measured
+// slower at 8 to 32 tables).
 template <int S, int NW = kFusedThreads / 64>
 __device__ __forceinline__ void mlp_layer_any(const float* in, int ldi, int K, const float* Wp, const float* bias,
                                               int N, bool relu, float* out, int ldo) {
+    if (wide_tiles(N)) {
+        const int tw = ((N + 31) / 32 + NW - 1) / NW;
+        const int nkc = (K + 7) >> 3;
+#define DLRM_WIDE(TW_, KU_, PD_)                                                     \
+    {                                                                                \
+        mlp_layer_wide<S, TW_, KU_, PD_, NW>(in, ldi, K, Wp, bias, N, relu, out, ldo); \
+        return;                                                                      \
+    }
+        if (tw <= 1) DLRM_WIDE(1, 4, 2)
+        if (nkc <= 1) DLRM_WIDE(2, 1, 1)
+        if (S > 8 || tw <= 2) DLRM_WIDE(2, 1, 6)
+        DLRM_WIDE(4, 1, 6)
+#undef DLRM_WIDE
+    }
     const int ntile = (N + 15) >> 4;
     const int tw = (ntile + NW - 1) / NW;
 #define DLRM_LAYER(TW_, KU_, PD_)                                               \
@@ -274,21 +410,32 @@ __device__ __forceinline__ void last_layer(const float* in, int ldi, int K, cons
 // Output n = 16 t + 4 fg + e sits in lanes 16 fg + 4 kg + e of tile t, which
 // hold its inputs 4 kg .. 4 kg + 3 (zero past the input width).
 template <int NPRE>
-__device__ __forceinline__ void first_layer_weights(const float* __restrict__ Wp, int N, int j, int nt,
+__device__ __forceinline__ void first_layer_weights(const float* __restrict__ Wp, int N, int K, int j, int nt,
                                                     floatx4 (&w)[NPRE][4]) {
 #pragma unroll
     for (int i = 0; i < NPRE; ++i) {
         const int n0 = j + i * nt;
         const int n = n0 < N ? n0 : 0;
-        const int t = n >> 4, r = n & 15;
+        if (wide_tiles(N)) {
+            const int t = n >> 5, r = n & 31;
+            const int nkc = (K + 7) >> 3;
 #pragma unroll
-        for (int kg = 0; kg < 4; ++kg)
-            w[i][kg] = ld_global<floatx4>(Wp + ((size_t)t * 64 + 16 * (r >> 2) + 4 * kg + (r & 3)) * 4);
+            for (int kg = 0; kg < 4; ++kg) {
+                const int c = kg >> 1;
+                w[i][kg] = c < nkc ? ld_global<floatx4>(Wp + (((size_t)t * nkc + c) * 64 + 8 * (r >> 2) + 4 * (kg & 1) + (r & 3)) * 4)
+                                   : floatx4{0.f, 0.f, 0.f, 0.f};
+            }
+        } else {
+            const int t = n >> 4, r = n & 15;
+#pragma unroll
+            for (int kg = 0; kg < 4; ++kg)
+                w[i][kg] = ld_global<floatx4>(Wp + ((size_t)t * 64 + 16 * (r >> 2) + 4 * kg + (r & 3)) * 4);
+        }
     }
 }
 
 template <int S, int NPRE>
-__device__ __forceinline__ void first_layer_valu(const float* in, int ldi, const float* __restrict__ Wp,
+__device__ __forceinline__ void first_layer_valu(const float* in, int ldi, int K0, const float* __restrict__ Wp,
                                                  const float* bias, int N, float* out, int ldo, int t0, int nt,
                                                  const floatx4 (&wpre)[NPRE][4]) {
     const int j = threadIdx.x - t0;
@@ -307,7 +454,7 @@ __device__ __forceinline__ void first_layer_valu(const float* in, int ldi, const
             for (int kg = 0; kg < 4; ++kg) w[kg] = wpre[i < NPRE ? i : 0][kg];
         } else {
             floatx4 wl[1][4];
-            first_layer_weights<1>(Wp, N, n, 0, wl);
+            first_layer_weights<1>(Wp, N, K0, n, 0, wl);
 #pragma unroll
             for (int kg = 0; kg < 4; ++kg) w[kg] = wl[0][kg];
         }
@@ -437,12 +584,12 @@ __global__ __launch_bounds__(kFusedThreads) void fused_forward_kernel(FusedArgs 
         __syncthreads();
         if (wave < kTeamWaves) {
             floatx4 w0[2][4];
-            if (valu0) first_layer_weights<2>(fa.bot.w[0], fa.bot.dim[1], tid, 64 * kTeamWaves, w0);
+            if (valu0) first_layer_weights<2>(fa.bot.w[0], fa.bot.dim[1], fa.bot.dim[0], tid, 64 * kTeamWaves, w0);
             load_dense_and_tail(64 * kTeamWaves);
             team_barrier(team_ctr, 1);
             for (int l = 0; l < nbot; ++l) {
                 if (l == 0 && valu0)
-                    first_layer_valu<S, 2>(buf(cur), lda, fa.bot.w[0], bias_lds, fa.bot.dim[1], buf(cur ^ 1), lda, 0,
+                    first_layer_valu<S, 2>(buf(cur), lda, fa.bot.dim[0], fa.bot.w[0], bias_lds, fa.bot.dim[1], buf(cur ^ 1), lda, 0,
                                            64 * kTeamWaves, w0);
                 else
                     mlp_layer_any<S, kTeamWaves>(buf(cur), lda, fa.bot.dim[l], fa.bot.w[l], bias_lds + boff,
@@ -461,13 +608,13 @@ __global__ __launch_bounds__(kFusedThreads) void fused_forward_kernel(FusedArgs 
         __syncthreads();
     } else {
         floatx4 w0[1][4];
-        if (valu0) first_layer_weights<1>(fa.bot.w[0], fa.bot.dim[1], tid, NT, w0);
+        if (valu0) first_layer_weights<1>(fa.bot.w[0], fa.bot.dim[1], fa.bot.dim[0], tid, NT, w0);
         load_dense_and_tail(NT);
         gather_all(0, NT);
         __syncthreads();
         for (int l = 0; l < nbot; ++l) {
             if (l == 0 && valu0)
-                first_layer_valu<S, 1>(buf(cur), lda, fa.bot.w[0], bias_lds, fa.bot.dim[1], buf(cur ^ 1), lda, 0, NT,
+                first_layer_valu<S, 1>(buf(cur), lda, fa.bot.dim[0], fa.bot.w[0], bias_lds, fa.bot.dim[1], buf(cur ^ 1), lda, 0, NT,
                                        w0);
             else
                 mlp_layer_any<S>(buf(cur), lda, fa.bot.dim[l], fa.bot.w[l], bias_lds + boff, fa.bot.dim[l + 1], true,
@@ -578,12 +725,13 @@ static hipError_t launch_fused_t(const FusedArgs& fa, hipStream_t s) {
 }
 
 size_t packed_layer_floats(int N, int K) {
-    const size_t f = (size_t)((N + 15) / 16) * ((K + 15) / 16) * 256;
+    const size_t f = wide_tiles(N) ? (size_t)((N + 31) / 32) * ((K + 7) / 8) * 256
+                                   : (size_t)((N + 15) / 16) * ((K + 15) / 16) * 256;
     return (f + 63) / 64 * 64;  // each layer starts 256-byte aligned
 }
 
 hipError_t launch_pack_layer(const float* W, int N, int K, float* packed, hipStream_t s) {
-    const int64_t total = (int64_t)((N + 15) / 16) * ((K + 15) / 16) * 64;
+    const int64_t total = (int64_t)(packed_layer_floats(N, K) / 4);
     hipLaunchKernelGGL(pack_layer_kernel, dim3((unsigned)((total + kBlock - 1) / kBlock)), dim3(kBlock), 0, s, W, N,
                        K, packed);
     return hipGetLastError();

@@ -360,10 +360,11 @@ dlrm_status_t dlrm_forward_layered(const dlrm_model_t* m, int64_t batch, const f
  * (see dlrm_forward_fused).  Host only.
  *
  * dlrm_pack_weights -- write them.  Every Linear layer but the one-output
- * last layer is stored as tiles of 16 output features x 16 inputs, each tile
- * as 64 lanes x 4 floats in the operand order of the kernel's matrix-core
- * instruction, zero past the layer's edges, so that one wave reads 1 KiB of
- * contiguous memory per load.  A tail holds the last layer's weights and bias
+ * last layer is stored in chunks of 64 lanes x 4 floats in the operand order
+ * of the kernel's matrix-core instruction, zero past the layer's edges, so
+ * that one wave reads 1 KiB of contiguous memory per load: layers of at most
+ * 128 outputs as tiles of 16 output features x 16 inputs, wider layers as
+ * tiles of 32 output features x 8 inputs.  A tail holds the last layer's weights and bias
  * and every hidden layer's bias, which the kernel copies to LDS at once.  packed: device, >= dlrm_pack_weights_bytes(m)
  * bytes, 256-byte aligned; written asynchronously on `stream`.  The caller
  * stores the pointer in m->packed_w and packs again after changing weights.

@@ -146,7 +146,10 @@ def test_fused_forward_rejects_models_outside_its_limits(lib, ln_bot, ln_top, T,
 def _packed_floats(ln):
     n = 0
     for k, o in zip(ln[:-1], ln[1:]):
-        f = ((o + 15) // 16) * ((k + 15) // 16) * 256
+        if o > 128:
+            f = ((o + 31) // 32) * ((k + 7) // 8) * 256
+        else:
+            f = ((o + 15) // 16) * ((k + 15) // 16) * 256
         n += (f + 63) // 64 * 64
     return n
 
@@ -156,11 +159,13 @@ def _packed_floats(ln):
     ([13, 512, 256, 64], [592, 512, 256, 1], 32, 64),
     ([4, 32, 16], [22, 32, 1], 3, 16),
     ([3, 37, 16], [22, 1], 3, 16),
+    ([5, 129, 128, 16], [22, 161, 97, 1], 3, 16),
 ])
 def test_pack_weights_bytes_formula(lib, ln_bot, ln_top, T, D):
-    """Every layer but the one-output last: ceil(N/16) x ceil(K/16) tiles of 256
-    floats, each layer rounded up to 256 bytes; then the tail of the last
-    layer's weights and bias and the hidden biases, each rounded up to 4 floats."""
+    """Every layer but the one-output last: for N <= 128 outputs ceil(N/16) x
+    ceil(K/16) tiles of 256 floats, for N > 128 ceil(N/32) x ceil(K/8); each
+    layer rounded up to 256 bytes; then the tail of the last layer's weights and
+    bias and the hidden biases, each rounded up to 4 floats."""
     m, keep = _model(ln_bot, ln_top, T, D)
     r4 = lambda v: (v + 3) // 4 * 4
     tail = r4(ln_top[-2]) + 4 + sum(r4(n) for n in ln_bot[1:]) + sum(r4(n) for n in ln_top[1:-1])
