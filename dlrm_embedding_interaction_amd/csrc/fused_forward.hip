@@ -398,14 +398,15 @@ __device__ __forceinline__ void last_layer(const float* in, int ldi, int K, cons
 }
 
 // The first bottom layer when its input is at most 16 wide (the dense
-// features; one 16-wide chunk per tile of the packed layout) runs on the
+// features) and it has at most 128 or more than 512 outputs runs on the
 // vector ALUs instead: thread j of the nt threads from t0 computes outputs
 // n = j, j + nt, ... for every sample, as a 16-term dot of the sample's
 // (zero-padded) input row with the output's packed weights, then bias and
 // ReLU.  Its weights are requested at kernel start (first_layer_weights), so
 // that they arrive during the bag gather; with 13 inputs the layer is a few
-// hundred instructions per thread, where a matrix-core pass would pay a ring
-// fill, an epilogue over 32 tiles and a barrier.
+// hundred instructions per thread, where a narrow matrix-core pass would pay a
+// ring fill, an epilogue over 32 tiles and a barrier.  (129..512 outputs take
+// first_layer_mfma below.)
 //
 // Output n = 16 t + 4 fg + e sits in lanes 16 fg + 4 kg + e of tile t, which
 // hold its inputs 4 kg .. 4 kg + 3 (zero past the input width).
@@ -479,6 +480,78 @@ __device__ __forceinline__ void first_layer_valu(const float* in, int ldi, int K
     }
 }
 
+// The first bottom layer on the matrix cores when it has at most 16 inputs
+// and 129..512 outputs (32-wide tiles): wave w of the nw waves that run it
+// takes tiles w, w + nw, ... (2 NPRE of them), and requests all of their
+// weights at kernel start -- two chunks of 8 inputs per tile, in the
+// registers the vector-ALU path would use -- so that they arrive during the
+// bag gather.  Then one pass of A-broadcast MFMAs as in mlp_layer_wide.
+template <int NPRE>
+__device__ __forceinline__ void first_layer_mfma_weights(const float* __restrict__ Wp, int N, int K, int wave, int nw,
+                                                         floatx4 (&w)[NPRE][4]) {
+    const int lane = threadIdx.x & 63;
+    const int ntile = (N + 31) >> 5;
+    const int nkc = (K + 7) >> 3;
+    const __amdgpu_buffer_rsrc_t wr = weight_rsrc(Wp, (uint32_t)ntile * nkc * 1024u);
+#pragma unroll
+    for (int i = 0; i < 4 * NPRE; ++i) {
+        const int t = wave + nw * (i >> 1), c = i & 1;
+        w[i >> 2][i & 3] =
+            buffer_load4(wr, t < ntile && c < nkc ? ((uint32_t)(t * nkc + c) * 64u + lane) * 16u : kOutOfRange);
+    }
+}
+
+template <int S, int NPRE>
+__device__ __forceinline__ void first_layer_mfma(const float* in, int ldi, const float* bias, int N, float* out,
+                                                 int ldo, int wave, int nw, const floatx4 (&w)[NPRE][4]) {
+    constexpr int SG = S / 8;
+    constexpr int TW = 2 * NPRE;
+    const int lane = threadIdx.x & 63;
+    const int m = lane >> 3;
+    const int s8 = lane & 7;
+    const int ntile = (N + 31) >> 5;
+    floatx4 acc[TW][SG][2];
+#pragma unroll
+    for (int u = 0; u < TW; ++u)
+#pragma unroll
+        for (int g = 0; g < SG; ++g) acc[u][g][0] = acc[u][g][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+    floatx4 a[2][SG][2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int g = 0; g < SG; ++g)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) a[c][g][h] = lds_load4(in + (8 * g + s8) * ldi + 8 * c + 4 * h);
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int u = 0; u < TW; ++u)
+#pragma unroll
+                for (int g = 0; g < SG; ++g) {
+                    const float wq = w[(2 * u + c) >> 2][(2 * u + c) & 3][q];
+                    acc[u][g][0] = __builtin_amdgcn_mfma_f32_4x4x1f32(wq, a[c][g][0][q], acc[u][g][0], 1, 0, 0);
+                    acc[u][g][1] = __builtin_amdgcn_mfma_f32_4x4x1f32(wq, a[c][g][1][q], acc[u][g][1], 1, 1, 0);
+                }
+#pragma unroll
+    for (int u = 0; u < TW; ++u) {
+        const int t = wave + nw * u;
+        if (t >= ntile) break;
+        const int n = 32 * t + 4 * m;
+        const floatx4 bv = n < N ? lds_load4(bias + n) : floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int g = 0; g < SG; ++g) {
+            const floatx4 v = acc[u][g][0] + acc[u][g][1] + bv;
+            floatx4 y;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) y[i] = n + i < N ? fmaxf(v[i], 0.f) : 0.f;
+            lds_store4(out + (8 * g + s8) * ldo + n, y);
+        }
+    }
+    zero_columns<S, kFusedThreads / NPRE>(out, ldo, (N + 31) & ~31, (N + 63) & ~63);
+}
+
 // Waves 0-3 of the block (the MLP team) wait here until all four have
 // arrived for the k-th time (k = 1, 2, ...): an arrival counter in LDS, read
 // with s_sleep between reads.  The other waves never take part, so the
@@ -530,6 +603,8 @@ __global__ __launch_bounds__(kFusedThreads) void fused_forward_kernel(FusedArgs 
     unsigned* const team_ctr = reinterpret_cast<unsigned*>(wlast + fa.n_small);
     const int wave = tid >> 6;
     const bool valu0 = fa.bot.dim[0] <= 16;  // the first layer on the vector ALUs
+    // ... or, 129 to 512 outputs wide, on the matrix cores
+    const bool mfma0 = valu0 && fa.bot.dim[1] > 128 && fa.bot.dim[1] <= 512;
 
     // 1. dense rows into buffer 0, zeros in its columns [n0, round_up(n0, 64))
     //    that the first layer's 64-wide k steps read past n0 (every layer
@@ -584,11 +659,17 @@ __global__ __launch_bounds__(kFusedThreads) void fused_forward_kernel(FusedArgs 
         __syncthreads();
         if (wave < kTeamWaves) {
             floatx4 w0[2][4];
-            if (valu0) first_layer_weights<2>(fa.bot.w[0], fa.bot.dim[1], fa.bot.dim[0], tid, 64 * kTeamWaves, w0);
+            if (mfma0)
+                first_layer_mfma_weights<2>(fa.bot.w[0], fa.bot.dim[1], fa.bot.dim[0], wave, kTeamWaves, w0);
+            else if (valu0)
+                first_layer_weights<2>(fa.bot.w[0], fa.bot.dim[1], fa.bot.dim[0], tid, 64 * kTeamWaves, w0);
             load_dense_and_tail(64 * kTeamWaves);
             team_barrier(team_ctr, 1);
             for (int l = 0; l < nbot; ++l) {
-                if (l == 0 && valu0)
+                if (l == 0 && mfma0)
+                    first_layer_mfma<S, 2>(buf(cur), lda, bias_lds, fa.bot.dim[1], buf(cur ^ 1), lda, wave, kTeamWaves,
+                                           w0);
+                else if (l == 0 && valu0)
                     first_layer_valu<S, 2>(buf(cur), lda, fa.bot.dim[0], fa.bot.w[0], bias_lds, fa.bot.dim[1], buf(cur ^ 1), lda, 0,
                                            64 * kTeamWaves, w0);
                 else
@@ -608,12 +689,17 @@ __global__ __launch_bounds__(kFusedThreads) void fused_forward_kernel(FusedArgs 
         __syncthreads();
     } else {
         floatx4 w0[1][4];
-        if (valu0) first_layer_weights<1>(fa.bot.w[0], fa.bot.dim[1], fa.bot.dim[0], tid, NT, w0);
+        if (mfma0)
+            first_layer_mfma_weights<1>(fa.bot.w[0], fa.bot.dim[1], fa.bot.dim[0], wave, NT / 64, w0);
+        else if (valu0)
+            first_layer_weights<1>(fa.bot.w[0], fa.bot.dim[1], fa.bot.dim[0], tid, NT, w0);
         load_dense_and_tail(NT);
         gather_all(0, NT);
         __syncthreads();
         for (int l = 0; l < nbot; ++l) {
-            if (l == 0 && valu0)
+            if (l == 0 && mfma0)
+                first_layer_mfma<S, 1>(buf(cur), lda, bias_lds, fa.bot.dim[1], buf(cur ^ 1), lda, wave, NT / 64, w0);
+            else if (l == 0 && valu0)
                 first_layer_valu<S, 1>(buf(cur), lda, fa.bot.dim[0], fa.bot.w[0], bias_lds, fa.bot.dim[1], buf(cur ^ 1), lda, 0, NT,
                                        w0);
             else
