@@ -426,6 +426,20 @@ def test_forward_bags_gathered_beside_the_bottom_mlp(ln_bot, hidden_top, D, B, b
     _forward_check(inp, on_gpu(inp), orc, path="fused")
 
 
+@pytest.mark.parametrize("T", [3, 9])
+@pytest.mark.parametrize("B", [77, 2100])
+@pytest.mark.parametrize("n0,n1", [(1, 129), (8, 200), (9, 512), (16, 160), (13, 511)])
+def test_forward_first_layer_on_the_matrix_cores(n0, n1, B, T, orc):
+    """A first bottom layer of at most 16 inputs and 129-512 outputs runs on the
+    matrix cores with its weights requested at kernel start: inputs that fill one
+    or two 8-wide chunks, outputs that end inside a 32-wide tile, 8 and 16 samples
+    per block (ragged last block), with the bags gathered before it or beside it."""
+    w = di.custom(f"first_{n0}_{n1}_{T}", B, n0, T, 700, 32, 1, (n0, n1, 32), hidden_top=(64,), cfg_id=29)
+    inp = di.make_inputs(w)
+    log(f"first layer {n0}->{n1} T={T} B={B}")
+    _forward_check(inp, on_gpu(inp), orc, path="fused")
+
+
 
 @pytest.mark.parametrize("path", ["fused", "layered"])
 def test_forward_zero_last_layer_gives_exactly_half(path):
