@@ -32,6 +32,11 @@
 //    frees the ring's registers and LDS for 4 waves per SIMD instead of 2:
 //    random row reads scale with the waves issuing them more than with the
 //    bytes each has in flight (batch 16384 x 32 tables: 41.4 -> 35.8 us);
+//  * the CU issues the oldest waves' requests first, so with 16 tables or
+//    more (a long copy per sample) each wave lowers its issue priority
+//    (s_setprio) with every sample it finishes: waves that are behind catch
+//    up instead of draining the launch alone (batch 16384 x 16 tables:
+//    17.9 -> 17.5 us);
 //  * because G is symmetric, the same registers are both MFMA operands: tile
 //    (I, J) multiplies feature block I by block J, and the tile above the
 //    diagonal is never formed (NB = 2: tiles (0,0), (1,0), (1,1));
@@ -285,6 +290,19 @@ __global__ __launch_bounds__(kGramThreads) __attribute__((amdgpu_waves_per_eu(LI
             // first copy (a later LDS read would wait for the copies).
 #pragma unroll 1
             for (int s = 0; s < ns; ++s) {
+                // A CU issues its oldest waves' requests first, so the waves
+                // dispatched last fall behind and finish the launch alone.
+                // From 16 tables (a long copy per sample) a wave's issue
+                // priority falls with the samples it has done, so that the
+                // waves behind catch up.
+                if constexpr (FP > 16) {
+                    switch (s) {
+                        case 0: __builtin_amdgcn_s_setprio(3); break;
+                        case 1: __builtin_amdgcn_s_setprio(2); break;
+                        case 2: __builtin_amdgcn_s_setprio(1); break;
+                        default: __builtin_amdgcn_s_setprio(0); break;
+                    }
+                }
                 int64_t pr[NLD];
 #pragma unroll
                 for (int k = 0; k < NLD; ++k) {
