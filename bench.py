@@ -312,8 +312,9 @@ def run_workload(torch, dl, di, w, dev, args):
 
     kernels = time_stages(torch, dl, model, inp, idx_sets, ws, w, args.kernel_reps,
                           fused=model.packed is not None and path == "fused", ib=args.index_bytes)
-    # the counter summary was taken with 8-byte indices
-    traffic = counted_traffic(w.name) if args.index_bytes == 8 else {}
+    # the counter summary holds 8-byte-index runs under the workload's name and
+    # 4-byte-index runs under name + "_i32"
+    traffic = counted_traffic(w.name if args.index_bytes == 8 else w.name + "_i32")
     reuse = w.dist == "zipf"
     stages = [k for k in kernels if k["name"] != "fused_forward"]
     roof_layered = roofline(stages, dominant=True, traffic=traffic, reuse=reuse)
@@ -574,7 +575,7 @@ def large_cells(torch, dl, di, dev, args, ceil):
         nbytes = B * T * w.bag * (D * 4 + ib) + B * T * ib + B * D * 4 + B * P * 4
         gbps = nbytes / (us * 1e-6) / 1e9
         cell = {"us": us, "bytes": nbytes, "GBps": gbps, "frac_of_peak": gbps / HBM_PEAK_GBPS}
-        tr = counted_traffic(w.name).get("emb_interact") if ib == 8 else None
+        tr = counted_traffic(w.name if ib == 8 else w.name + "_i32").get("emb_interact")
         if tr:
             cell["traffic"] = tr
             cell["counted_GBps"] = tr / (us * 1e-6) / 1e9
