@@ -626,23 +626,24 @@ __global__ __launch_bounds__(kFusedThreads) void fused_forward_kernel(FusedArgs 
 
     // 2. bags of this block's samples into feature rows 1..T, by threads
     //    t0 .. t0 + nt - 1
-    auto gather_all = [&](int t0, int nt) {
+    auto gather_u = [&](auto slots, int t0, int nt) {
+        constexpr int UU = decltype(slots)::value;  // bag slots per lane group and pass
         const int tt = tid - t0;
         const int lg = tt % G;
         const int g = tt / G;
         const int ng = nt / G;
         const int nbag = nb * T;
-        for (int qb = 0; qb < nbag; qb += ng * U) {
-            int q[U];
+        for (int qb = 0; qb < nbag; qb += ng * UU) {
+            int q[UU];
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
+            for (int u = 0; u < UU; ++u) {
                 const int qq = qb + u * ng + g;
                 q[u] = qq < nbag ? qq : -1;
             }
-            typename V::T acc[U][1];
-            gather_bags<4, G, 1, U, R>(fa.ta, T, D, fa.B, b0, q, lg, acc);
+            typename V::T acc[UU][1];
+            gather_bags<4, G, 1, UU, R>(fa.ta, T, D, fa.B, b0, q, lg, acc);
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
+            for (int u = 0; u < UU; ++u) {
                 if (q[u] < 0) continue;
                 const int s = q[u] / T;
                 const int t = q[u] - s * T;
@@ -650,6 +651,7 @@ __global__ __launch_bounds__(kFusedThreads) void fused_forward_kernel(FusedArgs 
             }
         }
     };
+    auto gather_all = [&](int t0, int nt) { gather_u(std::integral_constant<int, U>{}, t0, nt); };
 
     // 3. bottom MLP, ReLU after every layer
     int cur = 0;
@@ -688,16 +690,29 @@ __global__ __launch_bounds__(kFusedThreads) void fused_forward_kernel(FusedArgs 
         }
         __syncthreads();
     } else {
+        // Late gather: a last bottom layer of at most 64 outputs (4 tiles)
+        // leaves waves 4-7 idle, and they gather the bags beside it instead of
+        // all waves before the bottom MLP, when the block has more bags than
+        // the 8-wave gather's lane groups (measured at batch 2048: 5-7 tables
+        // -2.5 to -3.0 us; at one bag per lane group or fewer it loses up to
+        // 0.8 us, the gather then overlapping the kernel's start anyway)
+        const bool late = nbot >= 2 && fa.bot.dim[nbot] <= 64 && S * T > NT / G;
         floatx4 w0[1][4];
         if (mfma0)
             first_layer_mfma_weights<1>(fa.bot.w[0], fa.bot.dim[1], fa.bot.dim[0], wave, NT / 64, w0);
         else if (valu0)
             first_layer_weights<1>(fa.bot.w[0], fa.bot.dim[1], fa.bot.dim[0], tid, NT, w0);
         load_dense_and_tail(NT);
-        gather_all(0, NT);
+        if (!late) gather_all(0, NT);
         __syncthreads();
         for (int l = 0; l < nbot; ++l) {
-            if (l == 0 && mfma0)
+            if (late && l + 1 == nbot) {
+                if (wave < kTeamWaves)
+                    mlp_layer_any<S, kTeamWaves>(buf(cur), lda, fa.bot.dim[l], fa.bot.w[l], bias_lds + boff,
+                                                 fa.bot.dim[l + 1], true, buf(cur ^ 1), lda);
+                else
+                    gather_u(std::integral_constant<int, 4>{}, 64 * kTeamWaves, NT - 64 * kTeamWaves);
+            } else if (l == 0 && mfma0)
                 first_layer_mfma<S, 1>(buf(cur), lda, bias_lds, fa.bot.dim[1], buf(cur ^ 1), lda, wave, NT / 64, w0);
             else if (l == 0 && valu0)
                 first_layer_valu<S, 1>(buf(cur), lda, fa.bot.dim[0], fa.bot.w[0], bias_lds, fa.bot.dim[1], buf(cur ^ 1), lda, 0, NT,

@@ -440,6 +440,30 @@ def test_forward_first_layer_on_the_matrix_cores(n0, n1, B, T, orc):
     _forward_check(inp, on_gpu(inp), orc, path="fused")
 
 
+@pytest.mark.parametrize("T", [3, 5, 7])
+@pytest.mark.parametrize("B", [77, 2100])
+@pytest.mark.parametrize("bag", ["one", "ragged"])
+@pytest.mark.parametrize("ln_bot", [(13, 128, 64), (13, 512, 256, 64), (5, 96, 40, 64)])
+def test_forward_bags_gathered_beside_the_last_bottom_layer(ln_bot, bag, B, T, orc):
+    """With more bags per block than the gather's lane groups (5-7 tables at 8
+    samples per block, 3-7 at 16) and a last bottom layer of at most 64
+    outputs, waves 4-7 gather the bags while waves 0-3 run that layer: one-index
+    bags and ragged multi-index bags with empty ones, 8 and 16 samples per block
+    with a ragged last block; 3 tables at 8 samples per block keep the gather
+    before the bottom MLP."""
+    w = di.custom(f"late_{T}_{len(ln_bot)}_{bag}", B, ln_bot[0], T, 600, 64, 1, ln_bot, hidden_top=(96,),
+                  cfg_id=30)
+    inp = di.make_inputs(w)
+    if bag == "ragged":
+        gen = torch.Generator().manual_seed(31 + T)
+        for t in range(T):
+            off, n = di.ragged_bags(B, 6, 3100 + 10 * T + t, empty_frac=0.2)
+            inp.offsets[t] = off
+            inp.indices[t] = torch.randint(0, w.rows, (n,), generator=gen)
+    log(f"late gather T={T} B={B} bag={bag} ln_bot={ln_bot}")
+    _forward_check(inp, on_gpu(inp), orc, path="fused")
+
+
 
 @pytest.mark.parametrize("path", ["fused", "layered"])
 def test_forward_zero_last_layer_gives_exactly_half(path):
