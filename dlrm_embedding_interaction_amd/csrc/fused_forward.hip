@@ -653,6 +653,62 @@ __global__ __launch_bounds__(kFusedThreads) void fused_forward_kernel(FusedArgs 
     };
     auto gather_all = [&](int t0, int nt) { gather_u(std::integral_constant<int, U>{}, t0, nt); };
 
+    // Split gather (one bag slot per lane group): at kernel start one thread per
+    // bag reads its bounds and, for a bag of one index, that index, and leaves
+    // the row's address in the first 8 bytes of the bag's feature row (0: an
+    // empty bag; -1: a bag of several indices); later fetch_rows copies the
+    // rows there.
+    auto resolve_rows = [&]() {
+        const int nbag = nb * T;
+        if (tid < nbag) {
+            const int s = tid / T;
+            const int t = tid - s * T;
+            const int64_t b = b0 + s;
+            const int i32 = fa.ta.idx32;
+            const int64_t k0 = ld_index(fa.ta.off[t], b, i32);
+            const int64_t k1 = b + 1 < fa.B ? ld_index(fa.ta.off[t], b + 1, i32) : fa.ta.nidx[t];
+            int64_t addr = k1 == k0 ? 0 : -1;
+            if (k1 - k0 == 1) addr = reinterpret_cast<int64_t>(fa.ta.w[t] + ld_index(fa.ta.idx[t], k0, i32) * D);
+            lds_store8(reinterpret_cast<int64_t*>(feat + ((size_t)s * F + 1 + t) * LDR), addr);
+        }
+    };
+    // the rows of the resolved bags by threads t0 .. t0 + nt - 1, two bag slots
+    // per lane group; a wave holding a bag of several indices sums its bags in
+    // full instead
+    auto fetch_rows = [&](int t0, int nt) {
+        const int tt = tid - t0;
+        const int lg = tt % G;
+        const int g = tt / G;
+        const int ng = nt / G;
+        const int nbag = nb * T;
+        for (int qb = 0; qb < nbag; qb += 2 * ng) {
+            int q[2];
+            float* slot[2];
+            int64_t addr[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int qq = qb + u * ng + g;
+                q[u] = qq < nbag ? qq : -1;
+                const int s = q[u] >= 0 ? q[u] / T : 0;
+                const int t = q[u] >= 0 ? q[u] - s * T : 0;
+                slot[u] = feat + ((size_t)s * F + 1 + t) * LDR;
+                addr[u] = q[u] >= 0 ? lds_load8(reinterpret_cast<const int64_t*>(slot[u])) : 0;
+            }
+            typename V::T v[2][1];
+            if (__any(addr[0] < 0 || addr[1] < 0)) {
+                gather_bags<4, G, 1, 2, R>(fa.ta, T, D, fa.B, b0, q, lg, v);
+            } else {
+#pragma unroll
+                for (int u = 0; u < 2; ++u)
+                    v[u][0] = (addr[u] != 0 && lg * 4 < D) ? V::gload(reinterpret_cast<const float*>(addr[u]) + lg * 4)
+                                                          : V::zero();
+            }
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+                if (q[u] >= 0 && lg * 4 < D) V::store(slot[u] + lg * 4, v[u][0]);
+        }
+    };
+
     // 3. bottom MLP, ReLU after every layer
     int cur = 0;
     int boff = 0;  // this layer's biases in bias_lds
@@ -697,21 +753,29 @@ __global__ __launch_bounds__(kFusedThreads) void fused_forward_kernel(FusedArgs 
         // -2.5 to -3.0 us; at one bag per lane group or fewer it loses up to
         // 0.8 us, the gather then overlapping the kernel's start anyway)
         const bool late = nbot >= 2 && fa.bot.dim[nbot] <= 64 && S * T > NT / G;
+        // with one bag slot per lane group the gather is split instead: bounds
+        // and indices at kernel start, the rows beside that last layer
+        const bool split = U == 1 && R == 1 && nbot >= 2 && fa.bot.dim[nbot] <= 64 && S * T <= NT / G;
         floatx4 w0[1][4];
         if (mfma0)
             first_layer_mfma_weights<1>(fa.bot.w[0], fa.bot.dim[1], fa.bot.dim[0], wave, NT / 64, w0);
         else if (valu0)
             first_layer_weights<1>(fa.bot.w[0], fa.bot.dim[1], fa.bot.dim[0], tid, NT, w0);
         load_dense_and_tail(NT);
-        if (!late) gather_all(0, NT);
+        if (split)
+            resolve_rows();
+        else if (!late)
+            gather_all(0, NT);
         __syncthreads();
         for (int l = 0; l < nbot; ++l) {
-            if (late && l + 1 == nbot) {
+            if ((late || split) && l + 1 == nbot) {
                 if (wave < kTeamWaves)
                     mlp_layer_any<S, kTeamWaves>(buf(cur), lda, fa.bot.dim[l], fa.bot.w[l], bias_lds + boff,
                                                  fa.bot.dim[l + 1], true, buf(cur ^ 1), lda);
-                else
+                else if (late)
                     gather_u(std::integral_constant<int, 4>{}, 64 * kTeamWaves, NT - 64 * kTeamWaves);
+                else
+                    fetch_rows(64 * kTeamWaves, NT - 64 * kTeamWaves);
             } else if (l == 0 && mfma0)
                 first_layer_mfma<S, 1>(buf(cur), lda, bias_lds, fa.bot.dim[1], buf(cur ^ 1), lda, wave, NT / 64, w0);
             else if (l == 0 && valu0)

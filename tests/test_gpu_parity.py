@@ -464,6 +464,37 @@ def test_forward_bags_gathered_beside_the_last_bottom_layer(ln_bot, bag, B, T, o
     _forward_check(inp, on_gpu(inp), orc, path="fused")
 
 
+@pytest.mark.parametrize("T", [1, 2, 3])
+@pytest.mark.parametrize("B", [77, 2100])
+@pytest.mark.parametrize("bag", ["one", "mixed"])
+@pytest.mark.parametrize("ln_bot", [(13, 128, 64), (13, 512, 256, 64)])
+def test_forward_split_gather(ln_bot, bag, B, T, orc):
+    """With one bag slot per lane group, the single launch reads bag bounds and
+    indices at kernel start and the rows beside the last bottom layer: bags of
+    one index, and (mixed) tables of exactly B indices in empty, one- and
+    two-index bags, which the launch cannot tell from one-index bags and which
+    take the full gather for their wave; 8 and 16 samples per block, a ragged
+    last block."""
+    w = di.custom(f"split_{T}_{len(ln_bot)}_{bag}", B, ln_bot[0], T, 500, 64, 1, ln_bot, hidden_top=(80,),
+                  cfg_id=31)
+    inp = di.make_inputs(w)
+    if bag == "mixed":
+        gen = torch.Generator().manual_seed(57 + T)
+        for t in range(T):
+            # lengths 0 / 2 in pairs and 1 elsewhere: B indices in total
+            lens = torch.ones(B, dtype=torch.int64)
+            pick = torch.randperm(B - 1, generator=gen)[: B // 6]
+            lens[pick] = 0
+            lens[pick + 1] = lens[pick + 1] + 1
+            off = torch.zeros(B, dtype=torch.int64)
+            off[1:] = torch.cumsum(lens[:-1], 0)
+            inp.offsets[t] = off
+            inp.indices[t] = torch.randint(0, w.rows, (int(lens.sum()),), generator=gen)
+            assert int(lens.sum()) == B and int(lens.max()) >= 2
+    log(f"split gather T={T} B={B} bag={bag} ln_bot={ln_bot}")
+    _forward_check(inp, on_gpu(inp), orc, path="fused")
+
+
 
 @pytest.mark.parametrize("path", ["fused", "layered"])
 def test_forward_zero_last_layer_gives_exactly_half(path):
