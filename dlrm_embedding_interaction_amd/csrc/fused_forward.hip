@@ -26,7 +26,13 @@
 //      instruction covering 16 features x 4 samples x 4 k values; the 4 k
 //      groups are added afterwards with two DPP row rotations;
 //  * the bags are gathered with the same lane-group code as the standalone
-//    bag kernel and the dots reuse the interaction kernel's LDS routine;
+//    bag kernel, scheduled where waves would otherwise wait: from 8 tables
+//    by waves 4-7 beside the whole bottom MLP on waves 0-3; below that, when
+//    the last bottom layer has at most 64 outputs (waves 4-7 idle in it),
+//    either wholly beside that layer (more bags than lane groups) or split,
+//    bounds and indices at kernel start and the rows beside it;
+//  * the dots reuse the interaction kernel's LDS routine, or one 32x32x2
+//    MFMA tile per sample from 24 to 32 tables;
 //  * nothing leaves the block but the S sigmoid outputs.
 //
 // Samples are independent, so blocks never communicate; the weights of one
